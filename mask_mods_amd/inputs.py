@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs shared by the GPU path's tests/bench and the CPU oracle.
+
+This module holds no attention arithmetic. It only draws random numbers and
+encodes them as the 16/32-bit patterns that both sides consume, so that the
+HIP kernels and the oracle read exactly the same input values:
+
+* values ~ N(0, 1) in float32 from numpy's PCG64 (``default_rng(seed)``);
+* bf16 bits by round-to-nearest-even of the float32 bit pattern; f16 bits by
+  numpy's float32 -> float16 cast (also round-to-nearest-even);
+* exact decoding of those bits to float64 for the oracle.
+
+The workloads follow the pages' shapes: Q/K/V laid out [B, H, S, D] with D
+innermost (IREE issue #19015, example IR), and a decode mask [B, H, 1, L] that
+is 0 on valid positions and -inf on a random trailing pad.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+# f16 bit patterns of the two additive-mask values used by the decode workload
+F16_ZERO_BITS = np.uint16(0x0000)
+F16_NEG_INF_BITS = np.uint16(0xFC00)
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Encode float32 values in ``dtype``: uint16 bits for f16/bf16, uint32 for f32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "f32":
+        return x.view(np.uint32).copy()
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Decode bit patterns exactly to float64 (every f16/bf16/f32 value is a float64)."""
+    bits = np.ascontiguousarray(bits)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "f32":
+        return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def normal_bits(g: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0,1) float32 draws encoded in ``dtype``."""
+    return f32_to_bits(g.standard_normal(size=shape, dtype=np.float32), dtype)
+
+
+def attention_inputs(seed: int, B: int, Hq: int, Hkv: int, Sq: int, Skv: int, D: int,
+                     dtype: str) -> dict:
+    """Q [B,Hq,Sq,D], K and V [B,Hkv,Skv,D] as bit arrays, drawn in that order."""
+    g = rng(seed)
+    return {
+        "q": normal_bits(g, (B, Hq, Sq, D), dtype),
+        "k": normal_bits(g, (B, Hkv, Skv, D), dtype),
+        "v": normal_bits(g, (B, Hkv, Skv, D), dtype),
+        "dtype": dtype,
+    }
+
+
+def pad_lengths(g: np.random.Generator, B: int, L: int) -> np.ndarray:
+    """One trailing-pad length per sequence, uniform on {0, ..., L-1}."""
+    return g.integers(0, L, size=B, dtype=np.int64)
+
+
+def decode_inputs(seed: int, B: int, Hq: int, Hkv: int, lens, D: int, dtype: str,
+                  Scap: int | None = None, with_pad_mask: bool = True) -> dict:
+    """Decode workload: one query per head against a KV cache of capacity Scap.
+
+    ``lens`` holds each sequence's KV length (all <= Scap). q is [B,Hq,1,D], the
+    caches [B,Hkv,Scap,D]. When ``with_pad_mask``, an f16 additive mask
+    [B,Hq,1,Scap] is 0 on the first len_b - pad_b positions and -inf after them,
+    with pad_b ~ U{0..len_b-1} per sequence (the same for every head), so at least
+    one position stays valid. Positions at or beyond len_b hold random data that a
+    correct kernel never reads into the result.
+    """
+    lens = np.asarray(lens, dtype=np.int64).reshape(B)
+    if Scap is None:
+        Scap = int(lens.max())
+    assert (lens >= 0).all() and (lens <= Scap).all()
+    g = rng(seed)
+    out = {
+        "q": normal_bits(g, (B, Hq, 1, D), dtype),
+        "k": normal_bits(g, (B, Hkv, Scap, D), dtype),
+        "v": normal_bits(g, (B, Hkv, Scap, D), dtype),
+        "lens": lens.astype(np.int32),
+        "dtype": dtype,
+        "Scap": Scap,
+    }
+    if with_pad_mask:
+        pads = np.array([g.integers(0, max(int(n), 1)) for n in lens], dtype=np.int64)
+        mask = np.full((B, Hq, 1, Scap), F16_NEG_INF_BITS, dtype=np.uint16)
+        for b in range(B):
+            mask[b, :, :, : int(lens[b] - pads[b])] = F16_ZERO_BITS
+        out["mask"] = mask
+        out["pads"] = pads
+    return out
+
+
+def random_f16_bias(seed: int, shape) -> np.ndarray:
+    """Finite additive-mask bits: N(0,1) rounded to f16."""
+    return f32_to_bits(rng(seed).standard_normal(size=shape, dtype=np.float32), "f16")
+
+
+def sample_rows(seed: int, B: int, H: int, S: int, n_random: int = 64) -> np.ndarray:
+    """Flat row ids r = (b*H + h)*S + i for sampled parity at full size.
+
+    Every (b, h) contributes its first and last row; n_random more rows are drawn
+    uniformly over all rows. Sorted and unique.
+    """
+    g = rng(seed)
+    rows = []
+    for bh in range(B * H):
+        rows.append(bh * S)
+        rows.append(bh * S + S - 1)
+    rows.extend(g.integers(0, B * H * S, size=n_random).tolist())
+    return np.unique(np.asarray(rows, dtype=np.int64))

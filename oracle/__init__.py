@@ -1,0 +1,139 @@
+"""The oracle: a plain fp64 CPU attention (``attn_oracle.c``) and its ctypes binding.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py``; never by the product package, which
+shares no code with it. The C source states the definition it implements and
+where on the pages each part comes from.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point this at a deliberately broken build of the oracle (mutation check).
+_LIB_OVERRIDE = os.environ.get("MASKMODS_ORACLE_LIB")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_lp = ctypes.POINTER(ctypes.c_int64)
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _LIB_OVERRIDE or _LIB
+    if not _LIB_OVERRIDE and not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_fmix32.argtypes = [ctypes.c_uint32]
+    lib.oracle_fmix32.restype = ctypes.c_uint32
+    lib.oracle_row_dropped.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64]
+    lib.oracle_row_dropped.restype = ctypes.c_int
+    lib.oracle_alibi_slope.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.oracle_alibi_slope.restype = ctypes.c_double
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_attention.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _dp, _dp, _dp, ctypes.c_int,
+        ctypes.c_double, ctypes.c_int, _dp,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
+        _dp, ctypes.c_int64, _ip,
+        _lp, ctypes.c_int64, _dp, _dp,
+    ]
+    lib.oracle_attention.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def fmix32(x: int) -> int:
+    return int(load().oracle_fmix32(x & 0xFFFFFFFF))
+
+
+def row_dropped(seed: int, threshold: int, row: int) -> bool:
+    return bool(load().oracle_row_dropped(seed & 0xFFFFFFFF, threshold & 0xFFFFFFFF, row))
+
+
+def alibi_slope(h: int, H: int) -> float:
+    return float(load().oracle_alibi_slope(h, H))
+
+
+def max_threads() -> int:
+    return int(load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    load().oracle_set_threads(int(n))
+
+
+def _ptr(a, typ):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=False,
+              slopes=None, rowdrop=None, add_mask=None, lens=None, rows=None):
+    """Run the oracle.
+
+    q: float64 [B,Hq,Sq,D]; k, v: float64 [B,Hkv,kv_cap,D] (first ``Skv`` keys used,
+    default kv_cap). window: None or int >= 0. rowdrop: None or (seed, threshold).
+    add_mask: None or float64 [B,Hq,Sq,mask_ld]. lens: None or int [B].
+    rows: None (all rows; returns O [B,Hq,Sq,D], LSE [B,Hq,Sq]) or flat row ids
+    (b*Hq + h)*Sq + i (returns O [n,D], LSE [n]).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, kv_cap, Dk = k.shape
+    assert v.shape == k.shape and Bk == B and Dk == D
+    if Skv is None:
+        Skv = kv_cap
+    if slopes is not None:
+        slopes = np.ascontiguousarray(slopes, dtype=np.float64)
+        assert slopes.shape == (Hq,)
+    mask_ld = 0
+    if add_mask is not None:
+        add_mask = np.ascontiguousarray(add_mask, dtype=np.float64)
+        assert add_mask.shape[:3] == (B, Hq, Sq) and add_mask.shape[3] >= Skv
+        mask_ld = add_mask.shape[3]
+    if lens is not None:
+        lens = np.ascontiguousarray(lens, dtype=np.int32).reshape(B)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        n = rows.size
+    else:
+        n = B * Hq * Sq
+    out = np.zeros((n, D), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    seed, thr = (0, 0) if rowdrop is None else rowdrop
+    rc = load().oracle_attention(
+        B, Hq, Hkv, Sq, Skv, D, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), kv_cap,
+        float(scale), int(bool(alibi)), _ptr(slopes, _dp),
+        int(bool(causal)), -1 if window is None else int(window), int(rowdrop is not None),
+        seed & 0xFFFFFFFF, thr & 0xFFFFFFFF,
+        _ptr(add_mask, _dp), mask_ld, _ptr(lens, _ip),
+        _ptr(rows, _lp), n if rows is not None else 0, _ptr(out, _dp), _ptr(lse, _dp))
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments")
+    if rows is None:
+        return out.reshape(B, Hq, Sq, D), lse.reshape(B, Hq, Sq)
+    return out, lse

@@ -1,0 +1,193 @@
+/*
+ * attn_oracle.c -- the oracle: a plain, slow CPU attention in float64.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. The product (the HIP library and its
+ * Python binding) never calls it and shares no code with it.
+ *
+ * What it computes (flex_attention semantics as described on the pages):
+ *   For each batch b, query head h, query row i, with kv head hk = h / (Hq/Hkv)
+ *   (GQA groups of consecutive query heads share one K/V head -- the
+ *   enable_gqa operand of the torch-mlir flex_attention op, PR #4366 description):
+ *     s_j  = scale * sum_d Q[b,h,i,d] * K[b,hk,j,d]               (fp64)
+ *     s_j += slope_h * (j - i)           if the alibi score_mod is on; the mod
+ *                                        sees the already-scaled score
+ *                                        ("scale-then-mod", FlyDSL PR #931, Summary)
+ *     s_j += mask[b,h,i,j]               if an additive mask is given (decode
+ *                                        form of IREE issue #19015: the mask is an
+ *                                        operand of the attention op next to Q,K,V
+ *                                        and the scale, added to the scaled score)
+ *     kept_j = mask_mod(b,h,i,j) AND j < len_b ; s_j = -inf if not kept
+ *                                        (mask applied after the score_mod,
+ *                                        FlyDSL PR #931, Summary)
+ *   If no key is kept (or every kept s_j is -inf): O = 0, LSE = -inf
+ *   (the fully-masked-row guard, FlyDSL PR #931, Summary). Otherwise
+ *     M = max_j s_j,  w_j = exp(s_j - M),  Lsum = sum_j w_j,
+ *     O[b,h,i,:] = sum_j w_j V[b,hk,j,:] / Lsum,   LSE = M + ln(Lsum).
+ *
+ * mask_mod predicates (true = keep), AND-composed:
+ *   causal:          j <= i          (raw indices, top-left aligned when Sq != Skv)
+ *   sliding window:  |i - j| <= w    (inclusive; the pages' built-in pairs it with causal)
+ *   row drop:        fmix32(seed ^ ((b*Hq + h)*Sq + i)) >= threshold, else the
+ *                    whole row is masked. fmix32 is the 32-bit finalizer of
+ *                    Austin Appleby's MurmurHash3 (public domain).
+ * alibi slope for query head h of H: 2^(-8(h+1)/H) unless slopes are given.
+ *
+ * Inputs are float64 arrays holding the exact values of the bf16/f16/f32 inputs.
+ * Nothing here is blocked, fused, reordered or rounded beyond that definition.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+uint32_t oracle_fmix32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+int oracle_row_dropped(uint32_t seed, uint32_t threshold, int64_t row)
+{
+    return oracle_fmix32(seed ^ (uint32_t)row) < threshold;
+}
+
+double oracle_alibi_slope(int h, int H)
+{
+    return pow(2.0, -8.0 * (double)(h + 1) / (double)H);
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+typedef struct {
+    int B, Hq, Hkv, Sq, Skv, D, kv_cap;
+    const double *q, *k, *v;
+    double scale;
+    int alibi;
+    const double *slopes;
+    int causal, window, rowdrop;
+    uint32_t seed, threshold;
+    const double *add_mask;
+    int64_t mask_ld;
+    const int32_t *lens;
+} problem;
+
+/* One query row. s: scratch of Skv doubles. o: D outputs. */
+static void attend_row(const problem *p, int b, int h, int i, double *s, double *o, double *lse)
+{
+    const int group = p->Hq / p->Hkv;
+    const int hk = h / group;
+    const int64_t row = ((int64_t)b * p->Hq + h) * p->Sq + i;
+    const double *qi = p->q + row * p->D;
+    const double *kb = p->k + ((int64_t)b * p->Hkv + hk) * p->kv_cap * p->D;
+    const double *vb = p->v + ((int64_t)b * p->Hkv + hk) * p->kv_cap * p->D;
+    const int len = p->lens ? p->lens[b] : p->Skv;
+    const int dropped = p->rowdrop && oracle_row_dropped(p->seed, p->threshold, row);
+    const double slope = p->alibi ? (p->slopes ? p->slopes[h] : oracle_alibi_slope(h, p->Hq)) : 0.0;
+
+    double M = -INFINITY;
+    for (int j = 0; j < p->Skv; ++j) {
+        int keep = !dropped && j < len;
+        if (p->causal && !(j <= i)) keep = 0;
+        if (p->window >= 0 && !(abs(i - j) <= p->window)) keep = 0;
+        if (!keep) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        double dot = 0.0;
+        for (int d = 0; d < p->D; ++d) dot += qi[d] * kb[(int64_t)j * p->D + d];
+        double x = p->scale * dot;
+        if (p->alibi) x += slope * (double)(j - i);
+        if (p->add_mask) x += p->add_mask[row * p->mask_ld + j];
+        s[j] = x;
+        if (x > M) M = x;
+    }
+    for (int d = 0; d < p->D; ++d) o[d] = 0.0;
+    if (M == -INFINITY) {
+        *lse = -INFINITY;
+        return;
+    }
+    double Lsum = 0.0;
+    for (int j = 0; j < p->Skv; ++j) {
+        if (s[j] == -INFINITY) continue;
+        double w = exp(s[j] - M);
+        Lsum += w;
+        for (int d = 0; d < p->D; ++d) o[d] += w * vb[(int64_t)j * p->D + d];
+    }
+    for (int d = 0; d < p->D; ++d) o[d] /= Lsum;
+    *lse = M + log(Lsum);
+}
+
+/*
+ * Returns 0 on success, -1 on invalid arguments.
+ *   q      [B,Hq,Sq,D]        contiguous
+ *   k, v   [B,Hkv,kv_cap,D]   contiguous; keys 0..Skv-1 are used (Skv <= kv_cap)
+ *   window < 0 disables the sliding window
+ *   add_mask: NULL or additive bias, element (row, j) at add_mask[row*mask_ld + j]
+ *   lens:  NULL or per-batch key count (keys j >= lens[b] are masked)
+ *   rows:  NULL -> every row in order; else nrows flat row ids (b*Hq + h)*Sq + i
+ *   out [nrows, D], lse [nrows]
+ */
+int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                     const double *q, const double *k, const double *v, int kv_cap,
+                     double scale, int alibi, const double *slopes,
+                     int causal, int window, int rowdrop, uint32_t seed, uint32_t threshold,
+                     const double *add_mask, int64_t mask_ld, const int32_t *lens,
+                     const int64_t *rows, int64_t nrows, double *out, double *lse)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return -1;
+    if (Hq % Hkv != 0 || kv_cap < Skv) return -1;
+    if (!q || !k || !v || !out || !lse) return -1;
+    const int64_t total = (int64_t)B * Hq * Sq;
+    if (!rows) nrows = total;
+    problem p = {B, Hq, Hkv, Sq, Skv, D, kv_cap, q, k, v, scale, alibi, slopes,
+                 causal, window, rowdrop, seed, threshold, add_mask, mask_ld, lens};
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t n = 0; n < nrows; ++n) {
+                const int64_t r = rows ? rows[n] : n;
+                if (r < 0 || r >= total) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                const int i = (int)(r % Sq);
+                const int h = (int)((r / Sq) % Hq);
+                const int b = (int)(r / ((int64_t)Sq * Hq));
+                attend_row(&p, b, h, i, s, out + n * D, lse + n);
+            }
+        }
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
