@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X: fused attention forward + decode.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * forward, bf16, B=2 H=Hkv=32 D=128 S=8192, no mod, with LSE (the headline);
+  * decode, f16, B=1 H=32 D=128, KV length 32768, additive pad mask, with LSE.
+Inputs are seeded N(0,1) (mask_mods_amd.inputs) and resident in HBM before timing.
+
+Printed: one JSON line with the forward TFLOP/s as `value`, its roofline (MFMA
+bound) and the decode GB/s with its roofline (HBM bound), the other flex cases at
+S=8192 for context, and the CPU oracle timed on a bounded sample of the same
+forward workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+PAGES_NO_MOD_MI300X_TFLOPS = 470.1  # FlyDSL PR #931 report, no_mod at this workload (MI300X)
+
+FWD = dict(B=2, H=32, S=8192, D=128)
+DEC = dict(B=1, H=32, L=32768, D=128)
+FWD_KERNEL = "fwd_mfma_kernel"
+DEC_KERNELS = ("decode_split_kernel", "decode_merge_kernel")
+KERNEL_SOURCES = ["mask_mods_amd/csrc/fwd_mfma.h", "mask_mods_amd/csrc/common.h",
+                  "mask_mods_amd/csrc/decode.hip", "mask_mods_amd/csrc/kernels.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def fwd_flops(B, H, Sq, Skv, D, causal=False):
+    f = 4.0 * B * H * Sq * Skv * D
+    return f / 2 if causal else f
+
+
+def fwd_bytes(B, H, S, D, elt=2):
+    return 4 * B * H * S * D * elt + B * H * S * 4
+
+
+def dec_bytes(B, H, L, D, elt=2):
+    return B * H * L * D * elt * 2 + B * H * L * 2 + 2 * B * H * D * elt + B * H * 4
+
+
+def window_pairs(S, w):
+    """Visited (i, j) pairs of |i-j| <= w AND j <= i over an S x S square."""
+    return sum(min(i, w) + 1 for i in range(S))
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(kernel)
+    if not ent or ent.get("src_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(x, target_s=10.0):
+    """Time the oracle on random rows of the forward workload (bounded sample)."""
+    import oracle
+    from mask_mods_amd import inputs
+    B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+    qd, kd, vd = (inputs.bits_to_f64(x[n], "bf16") for n in ("q", "k", "v"))
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    g = np.random.default_rng(123)
+    threads = oracle.max_threads()
+    probe = g.integers(0, B * H * S, size=64)
+    t0 = time.perf_counter()
+    oracle.attention(qd, kd, vd, scale=scale, rows=probe)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(max(64 * target_s / dt, 64), 200000))
+    rows = g.integers(0, B * H * S, size=n)
+    t0 = time.perf_counter()
+    oracle.attention(qd, kd, vd, scale=scale, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = n * 4.0 * S * D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} random query rows of the B2 H32 D128 S8192 bf16 no-mod forward "
+                      f"(each row against all {S} keys), fp64, {dt:.1f} s; full workload "
+                      f"extrapolates to {B * H * S / (n / dt):.0f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards by (batch, head) with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mask_mods_amd as mm
+    from mask_mods_amd import inputs
+
+    mm.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dev_tensor(bits, dtype):
+        tt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tt).to(dev)
+
+    # ---- inputs (seeded, synthetic), resident in HBM
+    B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+    xf = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+    q, k, v = (dev_tensor(xf[n], "bf16") for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+
+    Bd, Hd, L, Dd = DEC["B"], DEC["H"], DEC["L"], DEC["D"]
+    xd = inputs.decode_inputs(1, Bd, Hd, Hd, [L], Dd, "f16")
+    dq, dk, dv = (dev_tensor(xd[n], "f16") for n in ("q", "k", "v"))
+    dmask = dev_tensor(xd["mask"], "f16")
+    dout = torch.empty_like(dq)
+    dlse = torch.empty(Bd, Hd, dtype=torch.float32, device=dev)
+    ws = torch.empty(mm.decode_workspace_size(Bd, Hd, L, Dd) // 4 + 4, dtype=torch.float32, device=dev)
+    dscale = 0.08837890625
+    torch.cuda.synchronize()
+
+    def fwd():
+        mm.attn_fwd(q, k, v, scale, out=out, lse=lse)
+
+    def dec():
+        mm.attn_decode(dq, dk, dv, L, dscale, mask=dmask, workspace=ws, out=dout, lse=dlse)
+
+    for _ in range(args.warmup):
+        fwd()
+        dec()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        dec()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fwd_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    flops = fwd_flops(B, H, S, S, D)
+    fwd_avg_s = fwd_ms.mean() * 1e-3
+    tflops = flops / fwd_avg_s / 1e12
+    dbytes = dec_bytes(Bd, Hd, L, Dd)
+    dec_avg_s = dec_ms.mean() * 1e-3
+    gbs = dbytes / dec_avg_s / 1e9
+
+    # ---- other flex cases at the same shape (context; same kernel family)
+    cases = {}
+    if not args.no_cases:
+        W = 256
+        specs = {
+            "causal": dict(causal=True),
+            "alibi": dict(score_mod=mm.SCORE_ALIBI),
+            "sliding_window": dict(window=W, mask_flags=mm.MASK_CAUSAL),
+            "causal_via_mask": dict(mask_flags=mm.MASK_CAUSAL),
+        }
+        for name, kw in specs.items():
+            for _ in range(3):
+                mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 10
+            e0.record(stream)
+            for _ in range(n):
+                mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / n * 1e-3
+            dense = fwd_flops(B, H, S, S, D)
+            if name in ("causal", "causal_via_mask"):
+                alg = dense / 2
+            elif name == "sliding_window":
+                alg = 4.0 * B * H * D * window_pairs(S, W)
+            else:
+                alg = dense
+            ent = {"us": round(t * 1e6, 1), "tflops_dense_equiv": round(dense / t / 1e12, 1),
+                   "tflops_algorithmic": round(alg / t / 1e12, 1)}
+            if name == "causal":
+                ent["tflops_causal_half"] = round(dense / 2 / t / 1e12, 1)
+            ent["latency_vs_no_mod"] = round(t / fwd_avg_s, 3)
+            cases[name] = ent
+
+    traffic_fwd = load_traffic(FWD_KERNEL)
+    traffic_dec = load_traffic("decode")
+    res = {
+        "metric": "attn fwd TFLOPS bf16 B2 H32 D128 S8192 (+% MFMA peak); decode KV GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PAGES_NO_MOD_MI300X_TFLOPS, 3),
+        "vs_baseline_ref": "pages' FlyDSL no_mod on MI300X (gfx942), 470.1 TFLOP/s: context, other hardware",
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fwd bf16 B2 H32 Hkv32 D128 S8192 no-mod +LSE; "
+                               "decode f16 B1 H32 D128 L32768 pad-mask +LSE",
+                   "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "fwd_ms": round(float(fwd_ms.mean()), 4),
+        "fwd_ms_std": round(float(fwd_ms.std()), 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_fwd, "kernel": FWD_KERNEL,
+                     "algorithmic": f"{flops:.4e} flop per launch (4*B*H*S*S*D)"},
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s", "us": round(dec_avg_s * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_dec,
+                         "kernel": "+".join(DEC_KERNELS),
+                         "algorithmic": f"{dbytes} bytes per call (K+V+mask+q+out+lse)"},
+        },
+        "cases_s8192": cases,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(xf, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

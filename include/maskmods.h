@@ -1,0 +1,154 @@
+/*
+ * maskmods.h -- C ABI of libmaskmods.so: fused flex-style attention for MI355X (gfx950).
+ *
+ * Two operations, both asynchronous on the caller's HIP stream:
+ *
+ *   mm_attn_fwd     O = softmax(mask_mod(score_mod(scale * Q K^T))) V, plus the
+ *                   row log-sum-exp. This is PyTorch's flex_attention operator as the
+ *                   torch-mlir PR "[TORCH] Added flex_attention hop function" states
+ *                   its operands (query, key, value, scale, enable_gqa, return_lse,
+ *                   score_mod, mask_mod), with the built-in mods of FlyDSL PR #931
+ *                   ("Add flex_attention (score_mod / mask_mod) on the generic
+ *                   flash-attention kernel", Summary): alibi score_mod, causal and
+ *                   sliding-window mask_mods, applied scale first, then score_mod,
+ *                   then mask_mod; fully masked rows give O = 0 and LSE = -inf.
+ *
+ *   mm_attn_decode  one query per head against a KV cache whose length is known
+ *                   only at run time, with an optional additive f16 mask: the
+ *                   decode attention of IREE issue #19015 ("[ROCM] Support dynamic
+ *                   key-value cache sequence length", example IR: Q [B,H,1,D],
+ *                   K/V [B,H,?,D], f16 scale, mask [B,H,1,?], f32 score region),
+ *                   extended to per-sequence lengths (the issue asks for a dynamic
+ *                   batch as well).
+ *
+ * Conventions shared by both calls
+ *   - Tensors are row-major [B, H, S, D] with D innermost (stride 1). Strides are
+ *     given in ELEMENTS for the b, h and s dimensions.
+ *   - All tensor pointers are DEVICE pointers owned by the caller and borrowed for
+ *     the call; they must stay valid until the work on `stream` completes. The
+ *     library allocates no device memory and keeps no state between calls.
+ *   - GQA: Hq must be a multiple of Hkv; query head h reads K/V head h / (Hq/Hkv).
+ *   - Index alignment: q_idx and kv_idx are raw positions (top-left aligned when
+ *     Sq != Skv).
+ *   - LSE is natural-log, fp32, contiguous [B, Hq, Sq]; pass NULL to skip it.
+ *   - Arguments are validated on the host before anything is launched; a rejected
+ *     call launches nothing and returns a negative mm_status. A launch failure
+ *     reported by the runtime returns MM_ERR_LAUNCH. Non-finite Q/K/V or a +inf/NaN
+ *     mask entry give undefined results.
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ */
+#ifndef MASKMODS_H
+#define MASKMODS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MM_OK = 0,
+    MM_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    MM_ERR_SHAPE = -2,       /* bad size (<=0, Hq % Hkv != 0, kv_len > Scap ...) */
+    MM_ERR_DTYPE = -3,       /* dtype not supported by this call                */
+    MM_ERR_UNSUPPORTED = -4, /* head dim or mod combination not built           */
+    MM_ERR_STRIDE = -5,      /* D stride is not 1 or a stride is negative       */
+    MM_ERR_LAUNCH = -6,      /* the HIP runtime reported a launch error         */
+    MM_ERR_WORKSPACE = -7    /* decode workspace NULL or too small              */
+} mm_status;
+
+typedef enum { MM_F32 = 0, MM_F16 = 1, MM_BF16 = 2 } mm_dtype;
+
+/* score_mod(score, b, h, q_idx, kv_idx) -> score, applied to the scaled score */
+typedef enum {
+    MM_SCORE_NONE = 0,
+    MM_SCORE_ALIBI = 1 /* score + slope_h * (kv_idx - q_idx) */
+} mm_score_mod;
+
+/* mask_mod(b, h, q_idx, kv_idx) -> keep; flags are AND-composed */
+enum {
+    MM_MASK_NONE = 0u,
+    MM_MASK_CAUSAL = 1u,  /* keep iff kv_idx <= q_idx                                  */
+    MM_MASK_WINDOW = 2u,  /* keep iff |q_idx - kv_idx| <= window (inclusive)           */
+    MM_MASK_ROWDROP = 4u  /* drop the whole row iff fmix32(seed ^ row) < threshold,
+                             row = (b*Hq + h)*Sq + q_idx; fmix32 = MurmurHash3's
+                             32-bit finalizer                                           */
+};
+
+typedef struct mm_mods {
+    int32_t score_mod;            /* mm_score_mod                                      */
+    uint32_t mask_flags;          /* OR of MM_MASK_*                                   */
+    int32_t window;               /* MM_MASK_WINDOW half-width, >= 0                   */
+    uint32_t rowdrop_seed;        /* MM_MASK_ROWDROP                                   */
+    uint32_t rowdrop_threshold;   /* MM_MASK_ROWDROP: ~threshold/2^32 of rows dropped  */
+    const float *alibi_slopes;    /* device fp32 [Hq], or NULL for 2^(-8(h+1)/Hq)      */
+} mm_mods;
+
+typedef struct mm_fwd_args {
+    const void *q;        /* [B, Hq, Sq, D]  dtype                                    */
+    const void *k;        /* [B, Hkv, Skv, D] dtype                                   */
+    const void *v;        /* [B, Hkv, Skv, D] dtype                                   */
+    void *out;            /* [B, Hq, Sq, D]  dtype                                    */
+    float *lse;           /* [B, Hq, Sq] fp32 contiguous, or NULL                     */
+    int32_t dtype;        /* mm_dtype: MM_BF16, MM_F16 (MFMA path) or MM_F32           */
+    int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128}                                 */
+    int64_t q_strides[3]; /* elements, for b, h, s                                    */
+    int64_t k_strides[3];
+    int64_t v_strides[3];
+    int64_t o_strides[3];
+    float scale;          /* multiplies Q K^T before any mod                          */
+    int32_t causal;       /* nonzero: same predicate as MM_MASK_CAUSAL                */
+    mm_mods mods;
+} mm_fwd_args;
+
+typedef struct mm_decode_args {
+    const void *q;           /* [B, Hq, 1, D] dtype                                   */
+    const void *k_cache;     /* [B, Hkv, Scap, D] dtype                               */
+    const void *v_cache;     /* [B, Hkv, Scap, D] dtype                               */
+    void *out;               /* [B, Hq, 1, D] dtype                                   */
+    float *lse;              /* [B, Hq] fp32 contiguous, or NULL                      */
+    const void *mask;        /* f16 additive mask [B, Hq, 1, Scap] or NULL; added to
+                                the scaled score; -inf masks a position              */
+    const int32_t *seq_lens; /* device int32 [B] (each 0..kv_len), or NULL (= kv_len) */
+    int32_t dtype;           /* MM_F16 or MM_BF16                                     */
+    int32_t B, Hq, Hkv, kv_len, Scap, D; /* D in {64, 128}; 0 <= kv_len <= Scap        */
+    float scale;             /* e.g. f16(1/sqrt(128)) = 0.08837890625                 */
+    int64_t q_strides[2];    /* elements, for b, h                                    */
+    int64_t kv_strides[3];   /* elements, for b, h, s (K and V share them)            */
+    int64_t o_strides[2];    /* elements, for b, h                                    */
+    int64_t mask_strides[2]; /* elements, for b, h (position stride is 1)             */
+    void *workspace;         /* device scratch, >= mm_attn_decode_workspace_size()    */
+    size_t workspace_bytes;
+    int32_t num_splits;      /* 0 = automatic; else the KV split count to use         */
+} mm_decode_args;
+
+/* Forward attention. Returns MM_OK or a negative mm_status. */
+mm_status mm_attn_fwd(const mm_fwd_args *args, void *stream);
+
+/* Bytes of device workspace mm_attn_decode needs for these sizes (0 if invalid).
+ * num_splits as in mm_decode_args (0 = automatic). */
+size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t kv_len, int32_t D,
+                                     int32_t num_splits);
+
+/* Decode attention (two launches on `stream`: split pass, then merge). */
+mm_status mm_attn_decode(const mm_decode_args *args, void *stream);
+
+/* Split count mm_attn_decode uses when num_splits == 0. */
+int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t kv_len);
+
+/* Static string for a status code. */
+const char *mm_status_str(int32_t status);
+
+/* sizeof of the argument structs, for bindings to check their mirrored layout. */
+size_t mm_fwd_args_size(void);
+size_t mm_decode_args_size(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t mm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MASKMODS_H */

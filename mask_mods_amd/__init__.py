@@ -1,0 +1,283 @@
+"""mask_mods_amd: flex-style fused attention for MI355X (gfx950).
+
+A thin ctypes binding over ``libmaskmods.so`` (C ABI in ``include/maskmods.h``).
+This layer only marshals arguments: it takes torch tensors for device memory and
+the current HIP stream, fills the argument struct and calls the library. Every
+step of the computation runs in the library's HIP kernels; there is no fallback.
+If the library is missing, importing works but every call raises.
+
+    from mask_mods_amd import attn_fwd, attn_decode
+    out, lse = attn_fwd(q, k, v, scale, causal=True)              # [B,H,S,D]
+    out, lse = attn_decode(q, k_cache, v_cache, kv_len, scale, mask=mask)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "attn_fwd", "attn_decode", "decode_workspace_size", "decode_auto_splits",
+    "MaskModsError", "library_path", "load_library",
+    "SCORE_NONE", "SCORE_ALIBI", "MASK_CAUSAL", "MASK_WINDOW", "MASK_ROWDROP",
+    "ROWDROP_5PCT",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmaskmods.so")
+
+MM_F32, MM_F16, MM_BF16 = 0, 1, 2
+SCORE_NONE, SCORE_ALIBI = 0, 1
+MASK_CAUSAL, MASK_WINDOW, MASK_ROWDROP = 1, 2, 4
+ROWDROP_5PCT = int(0.05 * 2 ** 32)  # threshold that drops ~5% of rows
+
+_STATUS = {
+    0: "MM_OK", -1: "MM_ERR_NULL", -2: "MM_ERR_SHAPE", -3: "MM_ERR_DTYPE",
+    -4: "MM_ERR_UNSUPPORTED", -5: "MM_ERR_STRIDE", -6: "MM_ERR_LAUNCH", -7: "MM_ERR_WORKSPACE",
+}
+
+
+class MaskModsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {_STATUS.get(status, status)}")
+
+
+class _Mods(ctypes.Structure):
+    _fields_ = [
+        ("score_mod", ctypes.c_int32),
+        ("mask_flags", ctypes.c_uint32),
+        ("window", ctypes.c_int32),
+        ("rowdrop_seed", ctypes.c_uint32),
+        ("rowdrop_threshold", ctypes.c_uint32),
+        ("alibi_slopes", ctypes.c_void_p),
+    ]
+
+
+_I64x3 = ctypes.c_int64 * 3
+_I64x2 = ctypes.c_int64 * 2
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("Skv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("q_strides", _I64x3), ("k_strides", _I64x3), ("v_strides", _I64x3), ("o_strides", _I64x3),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("mods", _Mods),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("mask", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("kv_len", ctypes.c_int32), ("Scap", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q_strides", _I64x2), ("kv_strides", _I64x3), ("o_strides", _I64x2), ("mask_strides", _I64x2),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmaskmods.so and check the struct layouts match this binding."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m mask_mods_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.mm_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+    lib.mm_attn_fwd.restype = ctypes.c_int32
+    lib.mm_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+    lib.mm_attn_decode.restype = ctypes.c_int32
+    lib.mm_attn_decode_workspace_size.argtypes = [ctypes.c_int32] * 5
+    lib.mm_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mm_attn_decode_auto_splits.argtypes = [ctypes.c_int32] * 3
+    lib.mm_attn_decode_auto_splits.restype = ctypes.c_int32
+    lib.mm_status_str.argtypes = [ctypes.c_int32]
+    lib.mm_status_str.restype = ctypes.c_char_p
+    lib.mm_fwd_args_size.restype = ctypes.c_size_t
+    lib.mm_decode_args_size.restype = ctypes.c_size_t
+    lib.mm_version.restype = ctypes.c_int32
+    if lib.mm_fwd_args_size() != ctypes.sizeof(FwdArgs):
+        raise RuntimeError("mm_fwd_args layout mismatch between library and binding")
+    if lib.mm_decode_args_size() != ctypes.sizeof(DecodeArgs):
+        raise RuntimeError("mm_decode_args layout mismatch between library and binding")
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: MM_F32, torch.float16: MM_F16, torch.bfloat16: MM_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("mask_mods_amd operates on device tensors only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if t.dim() >= 1 and t.stride(-1) != 1 and t.size(-1) > 1:
+            raise ValueError("the last (head) dimension must be contiguous")
+    return dev
+
+
+def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_slopes=None,
+             mask_flags=0, window=None, rowdrop=None, return_lse=True, out=None, lse=None):
+    """Fused attention forward.
+
+    q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (bf16, f16 or f32; D in {64,128}).
+    score_mod: SCORE_NONE or SCORE_ALIBI (or the string "alibi").
+    mask_flags: OR of MASK_CAUSAL / MASK_WINDOW / MASK_ROWDROP; ``window`` sets
+    MASK_WINDOW, ``rowdrop=(seed, threshold)`` sets MASK_ROWDROP.
+    Returns (out, lse) with lse fp32 [B,Hq,Sq] (None if return_lse is False).
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = _check_dev(q, k, v, out, lse, alibi_slopes)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q/k/v shapes or dtypes disagree")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq)):
+        raise ValueError("lse must be contiguous fp32 [B,Hq,Sq]")
+    if isinstance(score_mod, str):
+        score_mod = {"none": SCORE_NONE, "alibi": SCORE_ALIBI}[score_mod]
+    flags = int(mask_flags)
+    if window is not None:
+        flags |= MASK_WINDOW
+    seed, thr = 0, 0
+    if rowdrop is not None:
+        flags |= MASK_ROWDROP
+        seed, thr = rowdrop
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (Hq,) \
+                or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be contiguous fp32 [Hq]")
+    a = FwdArgs()
+    a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.dtype = _dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    a.q_strides = _I64x3(*q.stride()[:3])
+    a.k_strides = _I64x3(*k.stride()[:3])
+    a.v_strides = _I64x3(*v.stride()[:3])
+    a.o_strides = _I64x3(*out.stride()[:3])
+    a.scale = float(scale)
+    a.causal = 1 if causal else 0
+    a.mods.score_mod = int(score_mod)
+    a.mods.mask_flags = flags
+    a.mods.window = int(window) if window is not None else 0
+    a.mods.rowdrop_seed = seed & 0xFFFFFFFF
+    a.mods.rowdrop_threshold = thr & 0xFFFFFFFF
+    a.mods.alibi_slopes = alibi_slopes.data_ptr() if alibi_slopes is not None else None
+    st = lib.mm_attn_fwd(ctypes.byref(a), _stream_ptr(dev))
+    if st != 0:
+        raise MaskModsError(st, "mm_attn_fwd")
+    return out, (lse if return_lse else None)
+
+
+def decode_workspace_size(B, Hq, kv_len, D, num_splits=0) -> int:
+    return int(load_library().mm_attn_decode_workspace_size(B, Hq, kv_len, D, num_splits))
+
+
+def decode_auto_splits(B, Hq, kv_len) -> int:
+    return int(load_library().mm_attn_decode_auto_splits(B, Hq, kv_len))
+
+
+def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
+                return_lse=True, num_splits=0, workspace=None, out=None, lse=None):
+    """Decode attention: q [B,Hq,1,D] against caches [B,Hkv,Scap,D] (f16/bf16).
+
+    kv_len: number of cache positions in use (<= Scap). mask: optional f16
+    additive mask [B,Hq,1,Scap] (last dim contiguous). seq_lens: optional int32
+    device tensor [B] of per-sequence lengths (<= kv_len).
+    Returns (out [B,Hq,1,D], lse fp32 [B,Hq] or None).
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = _check_dev(q, k_cache, v_cache, mask, seq_lens, out, lse, workspace)
+    B, Hq, one, D = q.shape
+    Bk, Hkv, Scap, Dk = k_cache.shape
+    if one != 1 or Bk != B or Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("decode shapes disagree")
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q/k/v dtypes disagree")
+    if mask is not None and (mask.dtype != torch.float16 or mask.shape[0] != B or mask.shape[1] != Hq
+                             or mask.shape[-1] < kv_len):
+        raise ValueError("mask must be f16 [B,Hq,1,>=kv_len]")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != B):
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=q.dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = lib.mm_attn_decode_workspace_size(B, Hq, int(kv_len), D, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=dev)
+    a = DecodeArgs()
+    a.q, a.k_cache, a.v_cache, a.out = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.mask = mask.data_ptr() if mask is not None else None
+    a.seq_lens = seq_lens.data_ptr() if seq_lens is not None else None
+    a.dtype = _dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.kv_len, a.Scap, a.D = B, Hq, Hkv, int(kv_len), Scap, D
+    a.scale = float(scale)
+    a.q_strides = _I64x2(*q.stride()[:2])
+    a.kv_strides = _I64x3(*k_cache.stride()[:3])
+    a.o_strides = _I64x2(*out.stride()[:2])
+    a.mask_strides = _I64x2(*(mask.stride()[:2] if mask is not None else (0, 0)))
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.num_splits = int(num_splits)
+    st = lib.mm_attn_decode(ctypes.byref(a), _stream_ptr(dev))
+    if st != 0:
+        raise MaskModsError(st, "mm_attn_decode")
+    return out, (lse if return_lse else None)

@@ -1,0 +1,208 @@
+// api.cpp -- the C ABI (include/maskmods.h): argument validation and dispatch.
+//
+// Every check runs on the host before anything is launched, so a rejected call has no
+// effect on the device. Nothing here allocates device memory or keeps state.
+#include "maskmods.h"
+
+#include <math.h>
+
+#include "kernels.h"
+
+using namespace mm;
+
+namespace {
+
+constexpr int kMaxSplits = 256;
+constexpr int kMinKeysPerSplit = 256;
+constexpr int kTargetDecodeBlocks = 2048;  // ~8 workgroups per CU
+
+bool bad_strides(const int64_t *s, int n) {
+    for (int i = 0; i < n; ++i)
+        if (s[i] < 0) return true;
+    return false;
+}
+
+// 16-byte vector loads/stores on the 16-bit paths: pointers 16-byte aligned and every
+// stride a multiple of 8 elements.
+bool misaligned16(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+bool strides_not_mult8(const int64_t *s, int n) {
+    for (int i = 0; i < n; ++i)
+        if (s[i] % 8 != 0) return true;
+    return false;
+}
+
+int decode_splits(int32_t B, int32_t Hq, int32_t kv_len, int32_t requested) {
+    if (requested > 0) return requested;
+    if (kv_len <= 0) return 1;
+    const int64_t rows = (int64_t)B * Hq;
+    int64_t want = (kTargetDecodeBlocks + rows - 1) / rows;
+    const int64_t by_len = ((int64_t)kv_len + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
+    if (want > by_len) want = by_len;
+    if (want < 1) want = 1;
+    if (want > kMaxSplits) want = kMaxSplits;
+    return (int)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mm_version(void) { return 100; }
+
+size_t mm_fwd_args_size(void) { return sizeof(mm_fwd_args); }
+size_t mm_decode_args_size(void) { return sizeof(mm_decode_args); }
+
+const char *mm_status_str(int32_t st) {
+    switch (st) {
+        case MM_OK: return "ok";
+        case MM_ERR_NULL: return "required pointer is NULL";
+        case MM_ERR_SHAPE: return "invalid shape";
+        case MM_ERR_DTYPE: return "unsupported dtype";
+        case MM_ERR_UNSUPPORTED: return "unsupported head dim or mod";
+        case MM_ERR_STRIDE: return "invalid stride or alignment";
+        case MM_ERR_LAUNCH: return "kernel launch failed";
+        case MM_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
+    if (!a) return MM_ERR_NULL;
+    // empty tensors may legitimately have NULL data pointers
+    const bool no_rows = (int64_t)a->B * a->Hq * a->Sq == 0;
+    if ((!a->q || !a->out) && !no_rows) return MM_ERR_NULL;
+    if ((!a->k || !a->v) && (int64_t)a->B * a->Hkv * a->Skv != 0) return MM_ERR_NULL;
+    if (a->dtype != MM_F32 && a->dtype != MM_F16 && a->dtype != MM_BF16) return MM_ERR_DTYPE;
+    if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0) return MM_ERR_SHAPE;
+    if (a->Hq % a->Hkv != 0) return MM_ERR_SHAPE;
+    if (a->D != 64 && a->D != 128) return MM_ERR_UNSUPPORTED;
+    if (a->mods.score_mod != MM_SCORE_NONE && a->mods.score_mod != MM_SCORE_ALIBI) return MM_ERR_UNSUPPORTED;
+    if (a->mods.mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW | MM_MASK_ROWDROP))
+        return MM_ERR_UNSUPPORTED;
+    if ((a->mods.mask_flags & MM_MASK_WINDOW) && a->mods.window < 0) return MM_ERR_SHAPE;
+    if (!isfinite(a->scale)) return MM_ERR_SHAPE;
+    if (bad_strides(a->q_strides, 3) || bad_strides(a->k_strides, 3) || bad_strides(a->v_strides, 3) ||
+        bad_strides(a->o_strides, 3))
+        return MM_ERR_STRIDE;
+    if (a->dtype != MM_F32) {
+        if (misaligned16(a->q) || misaligned16(a->k) || misaligned16(a->v) || misaligned16(a->out))
+            return MM_ERR_STRIDE;
+        if (strides_not_mult8(a->q_strides, 3) || strides_not_mult8(a->k_strides, 3) ||
+            strides_not_mult8(a->v_strides, 3) || strides_not_mult8(a->o_strides, 3))
+            return MM_ERR_STRIDE;
+    } else {
+        if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->out) & 3u) return MM_ERR_STRIDE;
+    }
+    if (no_rows) return MM_OK;  // nothing to compute
+
+    FwdParams p = {};
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.o = a->out;
+    p.lse = a->lse;
+    p.B = a->B;
+    p.Hq = a->Hq;
+    p.Hkv = a->Hkv;
+    p.Sq = a->Sq;
+    p.Skv = a->Skv;
+    p.group = a->Hq / a->Hkv;
+    p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_ss = a->q_strides[2];
+    p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_ss = a->k_strides[2];
+    p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_ss = a->v_strides[2];
+    p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_ss = a->o_strides[2];
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    p.slopes = a->mods.alibi_slopes;
+    p.window = a->mods.window;
+    p.rowdrop = (a->mods.mask_flags & MM_MASK_ROWDROP) ? 1 : 0;
+    p.rd_seed = a->mods.rowdrop_seed;
+    p.rd_thr = a->mods.rowdrop_threshold;
+
+    int mask = 0;
+    if (a->causal || (a->mods.mask_flags & MM_MASK_CAUSAL)) mask |= MASK_CAUSAL;
+    if (a->mods.mask_flags & MM_MASK_WINDOW) mask |= MASK_WINDOW;
+    const bool alibi = a->mods.score_mod == MM_SCORE_ALIBI;
+    hipStream_t s = (hipStream_t)stream;
+
+    hipError_t e;
+    if (a->dtype == MM_F32) {
+        p.n_qtiles = 1;
+        e = launch_fwd_f32(p, a->D, alibi, mask, s);
+    } else {
+        p.n_qtiles = (a->Sq + kFwdBM - 1) / kFwdBM;
+        if ((int64_t)p.n_qtiles * a->Hq * a->B > 0x7fffffff) return MM_ERR_SHAPE;
+        if (a->dtype == MM_BF16)
+            e = a->D == 64 ? launch_fwd_mfma_bf16_d64(p, alibi, mask, s) : launch_fwd_mfma_bf16_d128(p, alibi, mask, s);
+        else
+            e = a->D == 64 ? launch_fwd_mfma_f16_d64(p, alibi, mask, s) : launch_fwd_mfma_f16_d128(p, alibi, mask, s);
+    }
+    return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
+}
+
+int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t kv_len) {
+    if (B <= 0 || Hq <= 0 || kv_len < 0) return 0;
+    return decode_splits(B, Hq, kv_len, 0);
+}
+
+size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t kv_len, int32_t D, int32_t num_splits) {
+    if (B <= 0 || Hq <= 0 || kv_len < 0 || (D != 64 && D != 128) || num_splits < 0 || num_splits > kMaxSplits)
+        return 0;
+    const int splits = decode_splits(B, Hq, kv_len, num_splits);
+    return (size_t)B * Hq * splits * (size_t)(D + 2) * sizeof(float);
+}
+
+mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
+    if (!a) return MM_ERR_NULL;
+    if (a->B != 0 && (!a->q || !a->out)) return MM_ERR_NULL;
+    if (a->B != 0 && a->kv_len > 0 && (!a->k_cache || !a->v_cache)) return MM_ERR_NULL;
+    if (a->dtype != MM_F16 && a->dtype != MM_BF16) return MM_ERR_DTYPE;
+    if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->kv_len < 0 || a->Scap < a->kv_len) return MM_ERR_SHAPE;
+    if (a->Hq % a->Hkv != 0) return MM_ERR_SHAPE;
+    if (a->D != 64 && a->D != 128) return MM_ERR_UNSUPPORTED;
+    if (a->num_splits < 0 || a->num_splits > kMaxSplits) return MM_ERR_UNSUPPORTED;
+    if (!isfinite(a->scale)) return MM_ERR_SHAPE;
+    if (bad_strides(a->q_strides, 2) || bad_strides(a->kv_strides, 3) || bad_strides(a->o_strides, 2) ||
+        bad_strides(a->mask_strides, 2))
+        return MM_ERR_STRIDE;
+    if (misaligned16(a->q) || misaligned16(a->k_cache) || misaligned16(a->v_cache))
+        return MM_ERR_STRIDE;
+    if (strides_not_mult8(a->q_strides, 2) || strides_not_mult8(a->kv_strides, 3)) return MM_ERR_STRIDE;
+    if (((uintptr_t)a->out & 1u) || ((uintptr_t)a->mask & 1u)) return MM_ERR_STRIDE;
+    if (a->B == 0) return MM_OK;
+
+    const int splits = decode_splits(a->B, a->Hq, a->kv_len, a->num_splits);
+    const size_t need = (size_t)a->B * a->Hq * splits * (size_t)(a->D + 2) * sizeof(float);
+    if (!a->workspace || a->workspace_bytes < need) return MM_ERR_WORKSPACE;
+    if (misaligned16(a->workspace)) return MM_ERR_WORKSPACE;
+
+    DecParams p = {};
+    p.q = a->q;
+    p.k = a->k_cache;
+    p.v = a->v_cache;
+    p.o = a->out;
+    p.lse = a->lse;
+    p.mask = (const uint16_t *)a->mask;
+    p.lens = a->seq_lens;
+    p.B = a->B;
+    p.Hq = a->Hq;
+    p.Hkv = a->Hkv;
+    p.kv_len = a->kv_len;
+    p.group = a->Hq / a->Hkv;
+    p.splits = splits;
+    p.chunk = a->kv_len > 0 ? (a->kv_len + splits - 1) / splits : 1;
+    p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1];
+    p.kv_sb = a->kv_strides[0]; p.kv_sh = a->kv_strides[1]; p.kv_ss = a->kv_strides[2];
+    p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1];
+    p.m_sb = a->mask_strides[0]; p.m_sh = a->mask_strides[1];
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    float *ws = (float *)a->workspace;
+    const size_t nrow = (size_t)a->B * a->Hq * splits;
+    p.ws_o = ws;
+    p.ws_m = ws + nrow * a->D;
+    p.ws_l = p.ws_m + nrow;
+
+    const hipError_t e = launch_decode(p, a->dtype, a->D, (hipStream_t)stream);
+    return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
+}
+
+}  // extern "C"

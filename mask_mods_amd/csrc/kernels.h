@@ -1,0 +1,59 @@
+// kernels.h -- parameter blocks and launchers shared between the C-ABI layer (api.cpp)
+// and the kernel translation units. Host-visible; no device code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mm {
+
+enum { MASK_CAUSAL = 1, MASK_WINDOW = 2 };
+
+// Forward attention, one launch. Strides are in elements.
+struct FwdParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, Hq, Hkv, Sq, Skv, group;
+    int64_t q_sb, q_sh, q_ss;
+    int64_t k_sb, k_sh, k_ss;
+    int64_t v_sb, v_sh, v_ss;
+    int64_t o_sb, o_sh, o_ss;
+    float scale_log2;      // scale * log2(e): scores are kept in base-2 units
+    const float *slopes;   // alibi slopes per query head (natural units) or nullptr
+    int window;            // MASK_WINDOW half width
+    int rowdrop;           // nonzero: rows with fmix32(seed ^ row) < thr are fully masked
+    uint32_t rd_seed, rd_thr;
+    int n_qtiles;          // query tiles per (b, h)
+};
+
+// Decode split pass + merge. Strides are in elements.
+struct DecParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    const uint16_t *mask;  // f16 additive mask or nullptr
+    const int32_t *lens;   // per-sequence lengths or nullptr
+    int B, Hq, Hkv, kv_len, group, splits, chunk;
+    int64_t q_sb, q_sh;
+    int64_t kv_sb, kv_sh, kv_ss;
+    int64_t o_sb, o_sh;
+    int64_t m_sb, m_sh;
+    float scale_log2;
+    float *ws_o;           // [B, Hq, splits, D] unnormalised partial outputs
+    float *ws_m;           // [B, Hq, splits] partial row max (base 2)
+    float *ws_l;           // [B, Hq, splits] partial row sum
+};
+
+// Query rows per forward workgroup on the MFMA path.
+constexpr int kFwdBM = 128;
+
+// dtype: 1 = f16, 2 = bf16 (the mm_dtype values)
+hipError_t launch_fwd_mfma_bf16_d64(const FwdParams &p, bool alibi, int mask, hipStream_t s);
+hipError_t launch_fwd_mfma_bf16_d128(const FwdParams &p, bool alibi, int mask, hipStream_t s);
+hipError_t launch_fwd_mfma_f16_d64(const FwdParams &p, bool alibi, int mask, hipStream_t s);
+hipError_t launch_fwd_mfma_f16_d128(const FwdParams &p, bool alibi, int mask, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams &p, int D, bool alibi, int mask, hipStream_t s);
+hipError_t launch_decode(const DecParams &p, int dtype, int D, hipStream_t s);
+
+}  // namespace mm

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, mirrors the struct layouts, and rejects bad arguments before any
+launch (no compute calls: these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mask_mods_amd as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "maskmods.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, STRIDE, LAUNCH, WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below is rejected on the host
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mm.load_library()
+    names = _declared_functions()
+    assert "mm_attn_fwd" in names and "mm_attn_decode" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts_match():
+    lib = mm.load_library()
+    assert lib.mm_fwd_args_size() == ctypes.sizeof(mm.FwdArgs)
+    assert lib.mm_decode_args_size() == ctypes.sizeof(mm.DecodeArgs)
+    assert lib.mm_version() >= 100
+
+
+def test_status_strings():
+    lib = mm.load_library()
+    for st in (OK, NULL, SHAPE, DTYPE, UNSUP, STRIDE, LAUNCH, WORKSPACE):
+        assert lib.mm_status_str(st)
+    assert lib.mm_status_str(12345) == b"unknown status"
+
+
+def _fwd(**kw):
+    a = mm.FwdArgs()
+    a.q = a.k = a.v = a.out = FAKE
+    a.dtype = 2
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = 1, 4, 2, 16, 16, 128
+    a.q_strides = mm._I64x3(4 * 16 * 128, 16 * 128, 128)
+    a.k_strides = mm._I64x3(2 * 16 * 128, 16 * 128, 128)
+    a.v_strides = mm._I64x3(2 * 16 * 128, 16 * 128, 128)
+    a.o_strides = mm._I64x3(4 * 16 * 128, 16 * 128, 128)
+    a.scale = 0.1
+    for key, val in kw.items():
+        if key.startswith("mods_"):
+            setattr(a.mods, key[5:], val)
+        else:
+            setattr(a, key, val)
+    return mm.load_library().mm_attn_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL),
+    (dict(out=None), NULL),
+    (dict(k=None), NULL),
+    (dict(q=None, Sq=0), OK),
+    (dict(k=None, v=None, Skv=0, B=0), OK),
+    (dict(dtype=7), DTYPE),
+    (dict(Hq=3), SHAPE),
+    (dict(Hkv=0), SHAPE),
+    (dict(Sq=-1), SHAPE),
+    (dict(Skv=-5), SHAPE),
+    (dict(D=96), UNSUP),
+    (dict(D=256), UNSUP),
+    (dict(mods_score_mod=9), UNSUP),
+    (dict(mods_mask_flags=8), UNSUP),
+    (dict(mods_mask_flags=2, mods_window=-1), SHAPE),
+    (dict(q_strides=mm._I64x3(-1, 0, 0)), STRIDE),
+    (dict(k_strides=mm._I64x3(100, 12, 128)), STRIDE),
+    (dict(q=FAKE + 2), STRIDE),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(B=0), OK),
+    (dict(Sq=0), OK),
+])
+def test_fwd_rejects_before_launch(kw, status):
+    assert _fwd(**kw) == status
+
+
+def test_fwd_null_args():
+    assert mm.load_library().mm_attn_fwd(None, None) == NULL
+
+
+def _dec(**kw):
+    a = mm.DecodeArgs()
+    a.q = a.k_cache = a.v_cache = a.out = FAKE
+    a.dtype = 1
+    a.B, a.Hq, a.Hkv, a.kv_len, a.Scap, a.D = 1, 32, 32, 100, 128, 128
+    a.scale = 0.08837890625
+    a.q_strides = mm._I64x2(32 * 128, 128)
+    a.kv_strides = mm._I64x3(32 * 128 * 128, 128 * 128, 128)
+    a.o_strides = mm._I64x2(32 * 128, 128)
+    a.workspace = FAKE
+    a.workspace_bytes = 1 << 30
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return mm.load_library().mm_attn_decode(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL),
+    (dict(v_cache=None), NULL),
+    (dict(dtype=0), DTYPE),
+    (dict(Hq=30, Hkv=8), SHAPE),
+    (dict(kv_len=200), SHAPE),
+    (dict(kv_len=-1), SHAPE),
+    (dict(D=80), UNSUP),
+    (dict(num_splits=-2), UNSUP),
+    (dict(num_splits=100000), UNSUP),
+    (dict(kv_strides=mm._I64x3(0, -128, 128)), STRIDE),
+    (dict(kv_strides=mm._I64x3(0, 128, 130)), STRIDE),
+    (dict(k_cache=FAKE + 8), STRIDE),
+    (dict(workspace=None), WORKSPACE),
+    (dict(workspace_bytes=16), WORKSPACE),
+    (dict(B=0), OK),
+])
+def test_decode_rejects_before_launch(kw, status):
+    assert _dec(**kw) == status
+
+
+def test_decode_workspace_and_splits():
+    # 1 x 32 heads x 64 splits x (128 + 2) floats
+    assert mm.decode_auto_splits(1, 32, 32768) == 64
+    assert mm.decode_workspace_size(1, 32, 32768, 128) == 32 * 64 * 130 * 4
+    assert mm.decode_workspace_size(1, 32, 32768, 128, num_splits=3) == 32 * 3 * 130 * 4
+    assert mm.decode_auto_splits(1, 32, 1) == 1
+    assert mm.decode_auto_splits(1, 32, 0) == 1
+    assert mm.decode_workspace_size(1, 32, 100, 96) == 0
+    # no more splits than 256-key chunks, at most 256 splits
+    for B, L in [(1, 1000), (8, 4096), (1, 10 ** 7), (64, 32768)]:
+        s = mm.decode_auto_splits(B, 32, L)
+        assert 1 <= s <= min(256, -(-L // 256))

@@ -1,0 +1,230 @@
+"""GPU parity of the forward path (mm_attn_fwd through the C ABI) against the oracle.
+
+Every case prints its parameters first so a failing GPU step names itself.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import (F32_ATOL, F32_RTOL, LSE_ATOL, LSE_RTOL, O_ATOL, O_RTOL, assert_parity,
+                     to_f64, to_torch)
+from mask_mods_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+WINDOW = 256
+RD_SEED = 20240
+
+
+def _run(B, Hq, Hkv, Sq, Skv, D, dtype, *, causal=False, mask_causal=False, window=None,
+         alibi=False, rowdrop=False, seed=0, rows=None, scale=None, slopes=None):
+    import torch
+    import mask_mods_amd as mm
+    print(f"[fwd] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal} "
+          f"mask_causal={mask_causal} window={window} alibi={alibi} rowdrop={rowdrop} seed={seed}",
+          flush=True)
+    x = inputs.attention_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
+    q, k, v = (to_torch(x[n], dtype) for n in ("q", "k", "v"))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale32 = float(np.float32(scale))
+    rd = (RD_SEED, inputs_threshold()) if rowdrop else None
+    out, lse = mm.attn_fwd(q, k, v, scale32, causal=causal,
+                           score_mod=mm.SCORE_ALIBI if alibi else mm.SCORE_NONE,
+                           mask_flags=mm.MASK_CAUSAL if mask_causal else 0,
+                           window=window, rowdrop=rd, alibi_slopes=slopes)
+    torch.cuda.synchronize()
+    qd, kd, vd = (inputs.bits_to_f64(x[n], dtype) for n in ("q", "k", "v"))
+    ref_slopes = None if slopes is None else slopes.double().cpu().numpy()
+    O, L = oracle.attention(qd, kd, vd, scale=scale32, causal=causal or mask_causal, window=window,
+                            alibi=alibi, slopes=ref_slopes, rowdrop=rd, rows=rows)
+    got_o, got_l = to_f64(out), to_f64(lse)
+    if rows is not None:
+        got_o = got_o.reshape(-1, D)[rows]
+        got_l = got_l.reshape(-1)[rows]
+    if dtype == "f32":
+        assert_parity(got_o, O, F32_ATOL, F32_RTOL, "O")
+        assert_parity(got_l, L, F32_ATOL, F32_RTOL, "LSE")
+    else:
+        assert_parity(got_o, O, O_ATOL, O_RTOL, "O")
+        assert_parity(got_l, L, LSE_ATOL, LSE_RTOL, "LSE")
+    return out, lse
+
+
+def inputs_threshold():
+    return int(0.05 * 2 ** 32)
+
+
+# ---------------------------------------------------------------- tiny fp32 (config 0)
+def test_tiny_f32_dense():
+    _run(1, 2, 2, 128, 128, 64, "f32", scale=0.125)
+
+
+@pytest.mark.parametrize("mods", [dict(causal=True), dict(alibi=True), dict(window=7, causal=True),
+                                  dict(window=20), dict(alibi=True, causal=True, rowdrop=True)])
+def test_f32_mods(mods):
+    _run(2, 4, 2, 100, 90, 128, "f32", **mods)
+
+
+# ---------------------------------------------------------------- the flex matrix
+CASES = {
+    "no_mod": dict(),
+    "causal": dict(causal=True),
+    "causal_via_mask": dict(mask_causal=True),
+    "alibi": dict(alibi=True),
+    "alibi_causal": dict(alibi=True, causal=True),
+    "sliding_window": dict(window=WINDOW, mask_causal=True),
+    "window_only": dict(window=100),
+    "rowdrop": dict(rowdrop=True),
+}
+
+
+@pytest.mark.parametrize("S", [250, 1024])
+@pytest.mark.parametrize("case", sorted(CASES))
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_flex_matrix(dtype, D, case, S):
+    _run(1, 2, 2, S, S, D, dtype, **CASES[case])
+
+
+@pytest.mark.parametrize("case", ["no_mod", "causal", "alibi", "sliding_window"])
+def test_multi_tile_384_batched(case):
+    _run(2, 3, 3, 384, 384, 128, "bf16", seed=3, **CASES[case])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gqa(dtype):
+    _run(2, 8, 2, 300, 300, 128, dtype, causal=True, alibi=True, seed=4)
+    _run(1, 8, 1, 129, 257, 64, dtype, window=33, seed=5)
+
+
+@pytest.mark.parametrize("shape,mods", [
+    ((200, 700), dict(alibi=True)),
+    ((700, 200), dict(causal=True)),
+    ((1024, 300), dict(window=WINDOW, mask_causal=True)),  # rows >= 556 see no key
+    ((65, 1000), dict(window=40)),
+    ((1, 513), dict()),
+    ((129, 1), dict(causal=True)),
+])
+def test_cross_attention(shape, mods):
+    Sq, Skv = shape
+    out, lse = _run(1, 4, 2, Sq, Skv, 128, "bf16", seed=6, **mods)
+    if "window" in mods and mods.get("mask_causal") and Sq > Skv + mods["window"]:
+        l = to_f64(lse)
+        assert np.all(l[:, :, Skv + mods["window"]:] == -np.inf)
+        assert np.all(to_f64(out)[:, :, Skv + mods["window"]:] == 0)
+
+
+def test_empty_kv_gives_zero_and_neg_inf():
+    import torch
+    import mask_mods_amd as mm
+    q = torch.randn(1, 2, 40, 128, device="cuda", dtype=torch.bfloat16)
+    k = torch.empty(1, 2, 0, 128, device="cuda", dtype=torch.bfloat16)
+    out, lse = mm.attn_fwd(q, k, k.clone(), 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(lse == -float("inf"))
+
+
+def test_empty_queries_is_noop():
+    import torch
+    import mask_mods_amd as mm
+    q = torch.empty(1, 2, 0, 64, device="cuda", dtype=torch.float16)
+    k = torch.randn(1, 2, 10, 64, device="cuda", dtype=torch.float16)
+    out, lse = mm.attn_fwd(q, k, k, 0.1)
+    assert out.shape == (1, 2, 0, 64) and lse.shape == (1, 2, 0)
+
+
+def test_strided_inputs():
+    """Q/K/V/O stored [B, S, H, D] and viewed as [B, H, S, D]."""
+    import torch
+    import mask_mods_amd as mm
+    B, H, S, D = 2, 4, 200, 128
+    x = inputs.attention_inputs(7, B, H, H, S, S, D, "bf16")
+    dev = {n: to_torch(x[n], "bf16") for n in ("q", "k", "v")}
+    strided = {n: t.transpose(1, 2).contiguous().transpose(1, 2) for n, t in dev.items()}
+    assert not strided["q"].is_contiguous()
+    out = torch.empty(B, S, H, D, device="cuda", dtype=torch.bfloat16).transpose(1, 2)
+    mm.attn_fwd(strided["q"], strided["k"], strided["v"], 0.0883883, causal=True, out=out)
+    ref, _ = mm.attn_fwd(dev["q"], dev["k"], dev["v"], 0.0883883, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_explicit_slopes_match_default():
+    import torch
+    H = 4
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32,
+                          device="cuda")
+    _run(1, H, H, 200, 200, 64, "bf16", alibi=True, slopes=slopes, seed=8)
+    slopes2 = torch.tensor([0.5, -0.25, 0.0, 1.5], dtype=torch.float32, device="cuda")
+    _run(1, H, H, 200, 200, 64, "f16", alibi=True, slopes=slopes2, seed=9)
+
+
+def test_causal_flag_equals_causal_mask_mod_and_deterministic():
+    import torch
+    import mask_mods_amd as mm
+    x = inputs.attention_inputs(10, 1, 4, 4, 777, 777, 128, "bf16")
+    q, k, v = (to_torch(x[n], "bf16") for n in ("q", "k", "v"))
+    o1, l1 = mm.attn_fwd(q, k, v, 0.1, causal=True)
+    o2, l2 = mm.attn_fwd(q, k, v, 0.1, mask_flags=mm.MASK_CAUSAL)
+    o3, l3 = mm.attn_fwd(q, k, v, 0.1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_large_window_equals_no_mask():
+    import torch
+    import mask_mods_amd as mm
+    x = inputs.attention_inputs(11, 1, 2, 2, 300, 300, 64, "f16")
+    q, k, v = (to_torch(x[n], "f16") for n in ("q", "k", "v"))
+    o1, l1 = mm.attn_fwd(q, k, v, 0.1)
+    o2, l2 = mm.attn_fwd(q, k, v, 0.1, window=299)
+    torch.cuda.synchronize()
+    assert torch.allclose(o1.float(), o2.float(), atol=1e-3) and torch.allclose(l1, l2, atol=1e-5)
+
+
+# ---------------------------------------------------------------- full-size, sampled rows
+def _sample(B, H, S, seed):
+    return inputs.sample_rows(seed, B, H, S, n_random=64)
+
+
+@pytest.mark.parametrize("S", [2048, 4096, 8192])
+@pytest.mark.parametrize("causal", [False, True])
+def test_config_dense_bf16_sampled(S, causal):
+    _run(2, 32, 32, S, S, 128, "bf16", causal=causal, seed=2, rows=_sample(2, 32, S, 2))
+
+
+@pytest.mark.parametrize("case", ["alibi", "sliding_window", "causal_via_mask"])
+def test_config_mods_bf16_8192_sampled(case):
+    S = 8192
+    _run(2, 32, 32, S, S, 128, "bf16", seed=3, rows=_sample(2, 32, S, 3), **CASES[case])
+
+
+@pytest.mark.parametrize("case", ["alibi", "sliding_window", "causal_via_mask"])
+def test_config_mods_bf16_d64_sampled(case):
+    S = 2048
+    _run(2, 32, 32, S, S, 64, "bf16", seed=3, rows=_sample(2, 32, S, 3), **CASES[case])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("window", [None, WINDOW])
+def test_config_gqa_cross_rowdrop(dtype, window):
+    import torch
+    B, Hq, Hkv, Sq, Skv = 2, 32, 8, 1024, 8192
+    rows = _sample(B, Hq, Sq, 4)
+    out, lse = _run(B, Hq, Hkv, Sq, Skv, 128, dtype, seed=4, rowdrop=True, window=window,
+                    mask_causal=window is not None, rows=rows)
+    # every dropped row, not only the sampled ones, is exactly 0 / -inf
+    thr = inputs_threshold()
+    ids = np.arange(B * Hq * Sq)
+    dropped = np.array([oracle.row_dropped(RD_SEED, thr, int(r)) for r in ids])
+    rate = dropped.mean()
+    print(f"rowdrop rate {rate:.4f}")
+    assert 0.04 < rate < 0.06
+    l = to_f64(lse).reshape(-1)
+    o = to_f64(out).reshape(-1, 128)
+    assert np.all(l[dropped] == -np.inf) and np.all(o[dropped] == 0)
+    assert np.all(np.isfinite(l[~dropped]))
