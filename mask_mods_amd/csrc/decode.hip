@@ -6,10 +6,11 @@
 // there are only B*H rows, far fewer than the 256 CUs, so the key range is cut into
 // `splits` chunks and each (split, head, batch) gets its own workgroup:
 //
-//   pass 1 (split): stream the chunk's K/V rows from HBM with 16-byte coalesced loads
-//     (D/8 lanes per key, 4 keys in flight per lane group), dot products in fp32
-//     reduced across the key's lanes, online softmax, and write the unnormalised
-//     partial output plus its (max, sum) to the workspace;
+//   pass 1 (split): stream the chunk's K/V rows from HBM with 16-byte coalesced,
+//     non-temporal loads (D/8 lanes per key, 8 keys in flight per lane group), dot
+//     products in fp32 (v_dot2 on the 16-bit inputs) reduced across the key's lanes
+//     with DPP row ops, online softmax, and write the unnormalised partial output plus
+//     its (max, sum) to the workspace;
 //   pass 2 (merge): per (b, h) rescale the partials to the common max and normalise:
 //     O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, LSE = (M + log2 L) ln 2.
 // A row with no visible key (empty sequence or all -inf mask) yields O = 0, LSE = -inf.
@@ -18,13 +19,49 @@
 
 namespace mm {
 
+// Sum over each aligned group of N lanes (N = 8 or 16) with DPP row operations; every
+// lane of the group receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 8 || N == 16, "group");
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+    if (N == 16)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+    return v;
+}
+
+// q.k over the lane's 8 dims in fp32 (products of 16-bit values are exact in fp32)
+__device__ __forceinline__ float dot8(u32x4 q, u32x4 k, F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // copy the elements out first: a bit_cast of a vector-element lvalue reads element 0
+        const uint32_t qi = q[i], ki = k[i];
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, qi), __builtin_bit_cast(h2, ki), acc, false);
+    }
+    return acc;
+}
+__device__ __forceinline__ float dot8(u32x4 q, u32x4 k, BF16) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t qi = q[i], ki = k[i];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, qi), __builtin_bit_cast(b2, ki), acc, false);
+    }
+    return acc;
+}
+
 template <typename TT, int D, bool MASKED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
-    constexpr int LPK = D / 8;       // lanes per key
+    constexpr int LPK = D / 8;       // lanes per key (16 bytes each)
     constexpr int KPW = 64 / LPK;    // keys per wave per step
     constexpr int NW = 4;
     constexpr int STEP = NW * KPW;   // keys per workgroup per step
-    constexpr int U = 4;             // steps in flight per iteration
+    constexpr int U = 8;             // steps in flight per iteration
     constexpr int SLOTS = NW * KPW;  // partial softmax states per workgroup
 
     __shared__ float sm_m[SLOTS], sm_l[SLOTS];
@@ -41,8 +78,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     const int j_begin = s * p.chunk;
     const int j_end = min(len, j_begin + p.chunk);
 
-    const uint16_t *qp = (const uint16_t *)p.q + b * p.q_sb + h * p.q_sh + 8 * c;
-    f32x8 qf = widen8(*(const u32x4 *)qp, TT{}) * p.scale_log2;
+    const u32x4 qv = *(const u32x4 *)((const uint16_t *)p.q + b * p.q_sb + h * p.q_sh + 8 * c);
+    const float c2 = p.scale_log2;
 
     const uint16_t *kbase = (const uint16_t *)p.k + b * p.kv_sb + hk * p.kv_sh + 8 * c;
     const uint16_t *vbase = (const uint16_t *)p.v + b * p.kv_sb + hk * p.kv_sh + 8 * c;
@@ -54,26 +91,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     for (int base = j_begin; base < j_end; base += STEP * U) {
         u32x4 kr[U], vr[U];
         uint16_t mk[U];
-        bool valid[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int j = base + u * STEP + slot;
-            valid[u] = j < j_end;
-            kr[u] = valid[u] ? *(const u32x4 *)(kbase + (int64_t)j * p.kv_ss) : u32x4{0, 0, 0, 0};
-            vr[u] = valid[u] ? *(const u32x4 *)(vbase + (int64_t)j * p.kv_ss) : u32x4{0, 0, 0, 0};
-            if (MASKED) mk[u] = valid[u] ? mbase[j] : (uint16_t)0;
+            const int j = min(base + u * STEP + slot, j_end - 1);  // tail lanes re-read a valid key
+            kr[u] = __builtin_nontemporal_load((const u32x4 *)(kbase + (int64_t)j * p.kv_ss));
+            vr[u] = __builtin_nontemporal_load((const u32x4 *)(vbase + (int64_t)j * p.kv_ss));
+            if (MASKED) mk[u] = mbase[j];
         }
         float t[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const f32x8 kf = widen8(kr[u], TT{});
-            float dot = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dot = fmaf(qf[e], kf[e], dot);
-#pragma unroll
-            for (int off = LPK / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
-            if (MASKED) dot += widen1(mk[u], F16{}) * kLog2e;
-            t[u] = valid[u] ? dot : -INFINITY;
+            float dot = group_sum<LPK>(dot8(qv, kr[u], TT{})) * c2;
+            if (MASKED) dot = fmaf(widen1(mk[u], F16{}), kLog2e, dot);
+            t[u] = base + u * STEP + slot < j_end ? dot : -INFINITY;
         }
         float mt = t[0];
 #pragma unroll
@@ -102,10 +132,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
 
     if (tid < D) {
         float M = -INFINITY;
-#pragma unroll 8
+#pragma unroll
         for (int k = 0; k < SLOTS; ++k) M = fmaxf(M, sm_m[k]);
         float Ls = 0.f, Od = 0.f;
         if (M != -INFINITY) {
+#pragma unroll
             for (int k = 0; k < SLOTS; ++k) {
                 const float mk2 = sm_m[k];
                 const float w = mk2 == -INFINITY ? 0.f : fast_exp2(mk2 - M);
@@ -122,26 +153,50 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     }
 }
 
+// One workgroup per (b, h): weights of all splits in parallel, then the weighted sum
+// over splits split across 256 threads (D dims x 256/D split groups).
 template <typename TT, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
+    constexpr int SG = 256 / D;  // split groups
+    __shared__ float sm_w[256];
+    __shared__ float sm_red[2][4];
+    __shared__ float sm_acc[SG][D];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t w0 = ((int64_t)b * p.Hq + h) * p.splits;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.ws_m[w0 + s]);
-    float Ls = 0.f, Od = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < p.splits; ++s) {
-            const float ms = p.ws_m[w0 + s];
-            const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-            Ls += p.ws_l[w0 + s] * w;
-            Od += p.ws_o[(w0 + s) * D + d] * w;
-        }
+    const int S = p.splits;  // <= 256
+
+    const float ms = tid < S ? p.ws_m[w0 + tid] : -INFINITY;
+    const float ls = tid < S ? p.ws_l[w0 + tid] : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0) sm_red[0][wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(sm_red[0][0], sm_red[0][1]), fmaxf(sm_red[0][2], sm_red[0][3]));
+    const float w = (ms == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(ms - M);
+    sm_w[tid] = w;
+    float Lp = ls * w;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
+    if (lane == 0) sm_red[1][wave] = Lp;
+    __syncthreads();
+    const float Ls = sm_red[1][0] + sm_red[1][1] + sm_red[1][2] + sm_red[1][3];
+
+    const int d = tid % D, sg = tid / D;
+    float acc = 0.f;
+    for (int s0 = sg; s0 < S; s0 += SG) acc = fmaf(sm_w[s0], p.ws_o[(w0 + s0) * D + d], acc);
+    sm_acc[sg][d] = acc;
+    __syncthreads();
+    if (tid < D) {
+        float Od = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < SG; ++g2) Od += sm_acc[g2][tid];
+        const bool live = Ls > 0.f;
+        uint16_t *op = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh;
+        op[tid] = narrow1(live ? Od / Ls : 0.f, TT{});
+        if (tid == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = live ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
     }
-    const bool live = Ls > 0.f;
-    const float val = live ? Od / Ls : 0.f;
-    uint16_t *op = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh;
-    op[d] = narrow1(val, TT{});
-    if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = live ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 template <typename TT, int D>
@@ -153,7 +208,7 @@ static hipError_t launch_decode_t(const DecParams &p, hipStream_t s) {
         decode_split_kernel<TT, D, false><<<g1, dim3(256), 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decode_merge_kernel<TT, D><<<dim3((unsigned)p.Hq, (unsigned)p.B), dim3(D), 0, s>>>(p);
+    decode_merge_kernel<TT, D><<<dim3((unsigned)p.Hq, (unsigned)p.B), dim3(256), 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -1,26 +1,32 @@
 // fwd_mfma.h -- flash-attention forward for gfx950 with flex mods (bf16 / f16 inputs).
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, query head); each wave owns
-// 32 rows. Keys/values stream through LDS in tiles of 64, double buffered, with the
-// next tile's global loads in flight while the current tile is computed.
+// 32 rows, two workgroups share a CU. Keys/values stream through LDS in tiles of 64
+// keys, double buffered: the next tile is copied global -> LDS by the DMA path
+// (global_load_lds_dwordx4, no VGPR staging) while the current tile is computed.
 //
 // Both products run on the 32x32x16 MFMA with fp32 accumulation, in transposed form
 // so that a lane always owns one query row:
-//   S^T[j][i] = sum_d K[j][d] Q[i][d]      A = K tile from LDS, B = Q^T kept in VGPRs
-//   O^T[d][i] += sum_j V^T[d][j] P^T[j][i] A = V^T tile from LDS, B = P^T from registers
+//   S^T[j][i] = sum_d K[j][d] Q[i][d]      A = K tile (ds_read_b128), B = Q^T in VGPRs
+//   O^T[d][i] += sum_j V^T[d][j] P^T[j][i] A = V^T read with ds_read_b64_tr_b16 from the
+//                                          row-major V tile, B = P^T from registers
 // In the C layout a lane holds column i = lane % 32 and 16 rows, so the softmax
 // reductions over keys are lane-local plus one exchange with lane ^ 32, and the
-// per-row rescale of O is a per-lane scalar multiply.
+// per-row rescale of O is a per-lane scalar multiply. The contraction index of
+// V^T P^T (the key) is consumed in the order the S^T accumulator hands keys to each
+// lane, so P^T needs no data movement.
 //
-// The contraction index of P^T V^T (the key) may be permuted freely as long as both
-// operands agree; V^T is written to LDS with its keys in the order the S^T
-// accumulator hands them to each lane, so P^T needs no data movement at all.
+// K and V tiles are stored row-major (one key per row) with the 16-byte chunks of each
+// row XOR-swizzled by the row index, which keeps both the K reads (32 rows, one chunk)
+// and the transposed V reads (4 rows, two chunks per 16 lanes) free of bank conflicts.
 //
-// Scores are kept in base-2 units (t = scale*log2(e)*q.k [+ slope*log2(e)*(j-i)]), so
-// the softmax uses the hardware exp2. Semantics (FlyDSL PR #931, Summary): the
-// score_mod sees the scaled score, the mask_mod is applied after it, and rows with no
-// kept key produce O = 0, LSE = -inf (running max clamped to 0 while it is -inf, and
-// a guarded 1/l in the epilogue).
+// Softmax: scores are kept in base-2 units (t = scale*log2(e)*q.k [+ slope*log2(e)*(j-i)]).
+// The running max is only raised when a tile's max exceeds it by more than 2^8 in
+// probability (lazy rescale): P then stays <= 256, exact in the final O / l. Row sums
+// are accumulated from the same 16-bit P values that feed the PV product (v_dot2).
+// Semantics (FlyDSL PR #931, Summary): score_mod sees the scaled score, the mask_mod is
+// applied after it, and rows with no kept key give O = 0, LSE = -inf (the running max
+// is clamped to 0 while it is -inf, and the epilogue guards 1/l).
 #pragma once
 
 #include "common.h"
@@ -28,21 +34,55 @@
 
 namespace mm {
 
-template <typename TT, int D, bool ALIBI, int MASK>
-__global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
-    constexpr int BM = kFwdBM, BN = 64;
-    constexpr int KS = D / 16;   // k-steps of Q K^T
-    constexpr int DB = D / 32;   // 32-row blocks of O^T
-    constexpr int NKB = BN / 32; // 32-key blocks of S^T per tile
-    constexpr int KLD = D + 8;   // K tile row stride (elements), padded against bank conflicts
-    constexpr int VLD = BN + 8;  // V^T tile row stride (elements)
-    constexpr int TILE = BN * KLD + D * VLD;
-    constexpr int KCH = BN * D / 8 / 256;     // 16-byte K chunks per thread per tile
-    constexpr int VUNITS = (BN / 4) * (D / 8); // 4-key x 8-dim V blocks per tile
-    typedef typename TT::vec8 V8;
-    static_assert(KCH >= 1 && VUNITS <= 256, "tile shape");
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+#define MM_LDS __attribute__((address_space(3)))
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE];
+// row sum helper: acc + p.x + p.y on the 16-bit pair that feeds the PV MFMA
+__device__ __forceinline__ float dot2_ones(uint32_t pair, float acc, BF16) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+__device__ __forceinline__ float dot2_ones(uint32_t pair, float acc, F16) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), ones, acc, false);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b, BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b, F16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+// Swizzled row-major tile of 16-bit elements, D per row.
+template <int D>
+struct Tile {
+    static constexpr int ROWB = 2 * D;  // bytes per key row
+    static constexpr int CH = D / 8;    // 16-byte chunks per row
+    __host__ __device__ static constexpr int swz(int r) {
+        return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((r >> 1) & 7);
+    }
+    __host__ __device__ static constexpr int off(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
+};
+
+template <typename TT, int D, bool ALIBI, int MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma_kernel(FwdParams p) {
+    constexpr int BM = kFwdBM, BN = 64;
+    constexpr int KS = D / 16;    // k-steps of Q K^T
+    constexpr int DB = D / 32;    // 32-row blocks of O^T
+    constexpr int NKB = BN / 32;  // 32-key blocks of S^T per tile
+    typedef Tile<D> TL;
+    constexpr int TILEB = BN * TL::ROWB;            // bytes of one K (or V) tile
+    constexpr int LOADS = TILEB / 1024 / 4;         // DMA instructions per wave per tile
+    constexpr int RPI = 1024 / TL::ROWB;            // rows per DMA instruction
+    constexpr float kRescale = 8.f;                 // lazy-rescale threshold (log2 units)
+    typedef typename TT::vec8 V8;
+    static_assert(LOADS >= 1, "tile shape");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILEB];  // [buf][K|V]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -89,67 +129,55 @@ __global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
 
     float slope2 = 0.f;
     if (ALIBI) slope2 = (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e;
+    const float c2 = p.scale_log2;
+
+    // ---- per-lane LDS offsets (bytes, within one tile) ----
+    // K (A operand of S^T): row 32*kb + l32, chunk 2*ks + hi
+    int koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = TL::off(l32, 2 * ks + hi);
+    // V^T via transpose reads: lane = 16*G + t reads row 16*ks + 8*m2 + 4*hi + t/4,
+    // dims 32*db + 16*(G%2) + 4*(t%4) .. +3; the 16 lanes then hold V[rows][d] transposed.
+    int voff[DB][2];
+    {
+        const int G = lane >> 4, t = lane & 15;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int r = 8 * m2 + 4 * hi + (t >> 2);
+                const int d = 32 * db + 16 * (G & 1) + 4 * (t & 3);
+                voff[db][m2] = TL::off(r, d >> 3) + 2 * (d & 7);
+            }
+    }
+
+    // ---- DMA of one K and one V tile into buffer `buf` ----
+    auto load_tile = [&](int kt, int buf) {
+        const int k0 = kt * BN;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int blk = wave * LOADS + i;          // 1 KB block of the tile
+            const int r = blk * RPI + lane / TL::CH;   // tile row this lane fetches
+            const int c = (lane % TL::CH) ^ TL::swz(r);  // global chunk landing in this slot
+            const int gr = min(k0 + r, p.Skv - 1);     // rows past the end re-read the last key
+            __builtin_amdgcn_global_load_lds((const void *)(kg + (int64_t)gr * p.k_ss + 8 * c),
+                                             (MM_LDS void *)(&smem[buf][0][blk * 1024]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vg + (int64_t)gr * p.v_ss + 8 * c),
+                                             (MM_LDS void *)(&smem[buf][1][blk * 1024]), 16, 0, 0);
+        }
+    };
 
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // ---- global -> registers -> LDS staging ----
-    u32x4 kreg[KCH];
-    u32x4 vreg[4];
-    auto load_tile = [&](int kt) {
-        const int k0 = kt * BN;
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int idx = tid + 256 * c;
-            const int j = idx / (D / 8), dc = idx % (D / 8);
-            const int jj = k0 + j;
-            kreg[c] = jj < p.Skv ? *(const u32x4 *)(kg + (int64_t)jj * p.k_ss + 8 * dc) : u32x4{0, 0, 0, 0};
-        }
-        if (tid < VUNITS) {
-            const int kgi = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int jj = k0 + 4 * kgi + r;
-                vreg[r] = jj < p.Skv ? *(const u32x4 *)(vg + (int64_t)jj * p.v_ss + 8 * dc) : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t *Ks = smem + buf * TILE;
-        uint16_t *Vt = Ks + BN * KLD;
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int idx = tid + 256 * c;
-            const int j = idx / (D / 8), dc = idx % (D / 8);
-            *(u32x4 *)(Ks + j * KLD + 8 * dc) = kreg[c];
-        }
-        if (tid < VUNITS) {
-            const int kgi = tid / (D / 8), dc = tid % (D / 8);
-            // within each 16-key block, 4-key groups 0,1,2,3 go to slots 0,2,1,3
-            const int g = kgi & 3;
-            const int pos = 16 * (kgi >> 2) + 4 * (((g & 1) << 1) | (g >> 1));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int w = e >> 1, sh = (e & 1) * 16;
-                const uint32_t a0 = (vreg[0][w] >> sh) & 0xFFFFu, a1 = (vreg[1][w] >> sh) & 0xFFFFu;
-                const uint32_t a2 = (vreg[2][w] >> sh) & 0xFFFFu, a3 = (vreg[3][w] >> sh) & 0xFFFFu;
-                *(u32x2 *)(Vt + (8 * dc + e) * VLD + pos) = u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
-            }
-        }
-    };
-
-    if (kt_lo < kt_hi) {
-        load_tile(kt_lo);
-        store_tile(0);
-    }
+    if (kt_lo < kt_hi) load_tile(kt_lo, 0);
     __syncthreads();
 
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int buf = (kt - kt_lo) & 1;
-        const bool more = kt + 1 < kt_hi;
-        if (more) load_tile(kt + 1);
+        if (kt + 1 < kt_hi) load_tile(kt + 1, buf ^ 1);
 
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
@@ -164,71 +192,96 @@ __global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
         }
 
         if (!skip) {
-            const uint16_t *Ks = smem + buf * TILE;
-            const uint16_t *Vt = Ks + BN * KLD;
+            const unsigned char *Kt = smem[buf][0];
+            const unsigned char *Vt = smem[buf][1];
             f32x16 sacc[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 sacc[kb] = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const V8 a = as_vec<V8>(*(const u32x4 *)(Ks + (32 * kb + l32) * KLD + 16 * ks + 8 * hi));
+                    const V8 a = as_vec<V8>(*(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[ks]));
                     sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
                 }
             }
-            // scale, score_mod, mask_mod; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4
+            // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4
             float mloc = -INFINITY;
+            // general: alibi, masking or a non-positive scale; plain: max of raw dots * scale
+            const bool general = ALIBI || need_mask || !(c2 > 0.f);
+            if (general) {
+                const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
-                    float t = sacc[kb][e] * p.scale_log2;
-                    if (ALIBI) t += slope2 * (float)(j - row);
-                    if (need_mask) {
-                        bool keep = j < p.Skv;
-                        if (MASK & MASK_CAUSAL) keep &= j <= row;
-                        if (MASK & MASK_WINDOW) keep &= abs(row - j) <= p.window;
-                        t = keep ? t : -INFINITY;
+                    for (int e = 0; e < 16; ++e) {
+                        const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
+                        float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
+                        if (need_mask) {
+                            const int j = k0 + 4 * hi + jo;
+                            bool keep = j < p.Skv;
+                            if (MASK & MASK_CAUSAL) keep &= j <= row;
+                            if (MASK & MASK_WINDOW) keep &= abs(row - j) <= p.window;
+                            t = keep ? t : -INFINITY;
+                        }
+                        sacc[kb][e] = t;
+                        mloc = fmaxf(mloc, t);
                     }
-                    sacc[kb][e] = t;
-                    mloc = fmaxf(mloc, t);
                 }
+            } else {
+                // scale > 0 commutes with the max
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
+                mloc *= c2;
             }
             mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            const float m_new = fmaxf(m_run, mloc);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;  // clamp: no (-inf) - (-inf)
-            const float alpha = fast_exp2(m_run - m_use);
+            // lazy rescale: raise the running max only when the tile exceeds it by > 2^8
+            if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescale)) {
+                const float m_new = fmaxf(m_run, mloc);
+                const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            // P = 2^(t - m) as 16-bit pairs; row sum from the same 16-bit values
+            uint32_t pp[NKB][8];
             float psum = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float pv = fast_exp2(sacc[kb][e] - m_use);
-                    sacc[kb][e] = pv;
-                    psum += pv;
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    float x0, x1;
+                    if (general) {
+                        x0 = fast_exp2(sacc[kb][2 * e2] - m_use);
+                        x1 = fast_exp2(sacc[kb][2 * e2 + 1] - m_use);
+                    } else {
+                        x0 = fast_exp2(fmaf(sacc[kb][2 * e2], c2, -m_use));
+                        x1 = fast_exp2(fmaf(sacc[kb][2 * e2 + 1], c2, -m_use));
+                    }
+                    pp[kb][e2] = pack2(x0, x1, TT{});
+                    psum = dot2_ones(pp[kb][e2], psum, TT{});
                 }
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            l_run += psum;
             // O^T += V^T P^T
 #pragma unroll
             for (int ks = 0; ks < BN / 16; ++ks) {
-                const f32x16 &s = sacc[ks >> 1];
-                const int o8 = 8 * (ks & 1);
-                const f32x8 pf32 = {s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3],
-                                    s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]};
-                const V8 pf = cvt8(pf32, TT{});
+                const int kb = ks >> 1, o4 = 4 * (ks & 1);
+                const V8 pf = as_vec<V8>(u32x4{pp[kb][o4], pp[kb][o4 + 1], pp[kb][o4 + 2], pp[kb][o4 + 3]});
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const V8 a = as_vec<V8>(*(const u32x4 *)(Vt + (32 * db + l32) * VLD + 16 * ks + 8 * hi));
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][0]));
+                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][1]));
+                    const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi4);
+                    const V8 a = as_vec<V8>(u32x4{a0[0], a0[1], a1[0], a1[1]});
                     oacc[db] = mfma32x32x16(a, pf, oacc[db]);
                 }
             }
         }
-        if (more) store_tile(buf ^ 1);
         __syncthreads();
     }
 
