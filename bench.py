@@ -105,6 +105,49 @@ def cpu_baseline(x, target_s=10.0):
             "seconds": dt}
 
 
+def profile_one(args, torch, mm, inputs, dev):
+    """Run one kernel family only (for rocprofv3 passes); prints a small JSON line."""
+    def dev_tensor(bits, dtype):
+        tt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tt).to(dev)
+
+    if args.only == "copy":
+        n = 1 << 29  # 2^29 fp16 = 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+        unit_bytes = 2 * n
+    elif args.only == "fwd":
+        B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        fn = lambda: mm.attn_fwd(q, k, v, scale, out=out, lse=lse)
+        unit_bytes = fwd_bytes(B, H, S, D)
+    else:
+        Bd, Hd, L, Dd = DEC["B"], DEC["H"], DEC["L"], DEC["D"]
+        x = inputs.decode_inputs(1, Bd, Hd, Hd, [L], Dd, "f16")
+        dq, dk, dv, dm = (dev_tensor(x[n], "f16") for n in ("q", "k", "v", "mask"))
+        ws = torch.empty(mm.decode_workspace_size(Bd, Hd, L, Dd) // 4 + 4, dtype=torch.float32, device=dev)
+        fn = lambda: mm.attn_decode(dq, dk, dv, L, 0.08837890625, mask=dm, workspace=ws)
+        unit_bytes = dec_bytes(Bd, Hd, L, Dd)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(args.steps, 1)
+    print(json.dumps({"only": args.only, "ms_per_call": round(ms, 4), "steps": args.steps,
+                      "algorithmic_bytes_per_call": unit_bytes,
+                      "src_hash": kernel_source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +156,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
+                    help="profiling aid: run just one kernel family (or a plain 1 GiB device copy "
+                         "used to calibrate the HBM byte counters) and print its timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -127,6 +173,8 @@ def main():
     mm.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only is not None:
+        return profile_one(args, torch, mm, inputs, dev)
 
     def dev_tensor(bits, dtype):
         tt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]

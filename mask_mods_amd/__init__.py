@@ -24,7 +24,8 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libmaskmods.so")
+# MASKMODS_LIB may point at another build of the library (e.g. a tuning variant)
+_LIB_PATH = os.environ.get("MASKMODS_LIB") or os.path.join(_PKG, "libmaskmods.so")
 
 MM_F32, MM_F16, MM_BF16 = 0, 1, 2
 SCORE_NONE, SCORE_ALIBI = 0, 1

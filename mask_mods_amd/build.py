@@ -38,8 +38,8 @@ SOURCES = [
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -50,17 +50,20 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(jobs: int | None = None, resource_usage: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, resource_usage: bool = False, defines=(), out: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source and link ``out``. ``defines``: extra -D macros (tuning variants)."""
+    os.makedirs(build_dir, exist_ok=True)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    extra += [f"-D{d}" for d in defines]
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

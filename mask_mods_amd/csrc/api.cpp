@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
-constexpr int kTargetDecodeBlocks = 2048;  // ~8 workgroups per CU
+constexpr int kTargetDecodeBlocks = 1024;  // ~4 workgroups per CU, one resident round
 
 bool bad_strides(const int64_t *s, int n) {
     for (int i = 0; i < n; ++i)
@@ -89,6 +89,10 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
             return MM_ERR_STRIDE;
         if (strides_not_mult8(a->q_strides, 3) || strides_not_mult8(a->k_strides, 3) ||
             strides_not_mult8(a->v_strides, 3) || strides_not_mult8(a->o_strides, 3))
+            return MM_ERR_STRIDE;
+        // the MFMA kernel addresses a 64-key tile with 32-bit byte offsets
+        if ((64 * a->k_strides[2] + a->D) * 2 >= ((int64_t)1 << 31) ||
+            (64 * a->v_strides[2] + a->D) * 2 >= ((int64_t)1 << 31))
             return MM_ERR_STRIDE;
     } else {
         if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->out) & 3u) return MM_ERR_STRIDE;

@@ -184,9 +184,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     const float Ls = sm_red[1][0] + sm_red[1][1] + sm_red[1][2] + sm_red[1][3];
 
     const int d = tid % D, sg = tid / D;
-    float acc = 0.f;
-    for (int s0 = sg; s0 < S; s0 += SG) acc = fmaf(sm_w[s0], p.ws_o[(w0 + s0) * D + d], acc);
-    sm_acc[sg][d] = acc;
+    const float *op0 = p.ws_o + w0 * D + d;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int s0 = sg;
+    for (; s0 + 7 * SG < S; s0 += 8 * SG) {  // 8 independent loads in flight
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(sm_w[s0 + u * SG], op0[(int64_t)(s0 + u * SG) * D], acc[u]);
+    }
+    for (; s0 < S; s0 += SG) acc[0] = fmaf(sm_w[s0], op0[(int64_t)s0 * D], acc[0]);
+    sm_acc[sg][d] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     __syncthreads();
     if (tid < D) {
         float Od = 0.f;

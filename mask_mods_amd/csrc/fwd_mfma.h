@@ -39,6 +39,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 #define MM_LDS __attribute__((address_space(3)))
+#ifndef MM_SETPRIO
+#define MM_SETPRIO 0
+#endif
+// wave priority while issuing MFMA blocks (helps the two waves of a SIMD alternate)
+#define MM_PRIO_HI() do { if (MM_SETPRIO) __builtin_amdgcn_s_setprio(1); } while (0)
+#define MM_PRIO_LO() do { if (MM_SETPRIO) __builtin_amdgcn_s_setprio(0); } while (0)
 
 // row sum helper: acc + p.x + p.y on the 16-bit pair that feeds the PV MFMA
 __device__ __forceinline__ float dot2_ones(uint32_t pair, float acc, BF16) {
@@ -54,6 +60,13 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, BF16) {
 }
 __device__ __forceinline__ uint32_t pack2(float a, float b, F16) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+// max of x over lanes l and l ^ 32 (the two halves holding one query row)
+__device__ __forceinline__ float row_max2(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
 }
 
 // Swizzled row-major tile of 16-bit elements, D per row.
@@ -82,7 +95,11 @@ void fwd_mfma_kernel(FwdParams p) {
     typedef typename TT::vec8 V8;
     static_assert(LOADS >= 1, "tile shape");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILEB];  // [buf][K|V]
+    // two K/V buffers as distinct LDS objects: the loop below is unrolled by two so each
+    // half reads one buffer while the DMA fills the other, and the compiler can see the
+    // reads never alias the in-flight copies (no early vmcnt wait).
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TILEB], vbuf0[TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[TILEB], vbuf1[TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -151,19 +168,47 @@ void fwd_mfma_kernel(FwdParams p) {
             }
     }
 
-    // ---- DMA of one K and one V tile into buffer `buf` ----
-    auto load_tile = [&](int kt, int buf) {
-        const int k0 = kt * BN;
+    // ---- DMA of one K and one V tile ----
+    // Each wave copies LOADS blocks of 1 KB per tile; block `blk` holds tile rows
+    // blk*RPI .. +RPI-1 and lane L lands in LDS slot L of the block: tile row
+    // r = blk*RPI + L/CH, chunk slot L%CH, which receives global chunk (L%CH) ^ swz(r).
+    // The lane's byte offset inside a tile is loop-invariant (32-bit; the host bounds
+    // 64*stride); full tiles add a wave-uniform base so the copy uses the
+    // scalar-base + vector-offset address form. The tile that crosses Skv clamps rows
+    // to the last key instead (their scores are masked).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t kgo[LOADS], vgo[LOADS];
+    int trow[LOADS], tchunk[LOADS];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int blk = wave * LOADS + i;          // 1 KB block of the tile
-            const int r = blk * RPI + lane / TL::CH;   // tile row this lane fetches
-            const int c = (lane % TL::CH) ^ TL::swz(r);  // global chunk landing in this slot
-            const int gr = min(k0 + r, p.Skv - 1);     // rows past the end re-read the last key
-            __builtin_amdgcn_global_load_lds((const void *)(kg + (int64_t)gr * p.k_ss + 8 * c),
-                                             (MM_LDS void *)(&smem[buf][0][blk * 1024]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vg + (int64_t)gr * p.v_ss + 8 * c),
-                                             (MM_LDS void *)(&smem[buf][1][blk * 1024]), 16, 0, 0);
+    for (int i = 0; i < LOADS; ++i) {
+        const int r = (wave_s * LOADS + i) * RPI + lane / TL::CH;
+        const int c = (lane % TL::CH) ^ TL::swz(r);
+        trow[i] = r;
+        tchunk[i] = c;
+        kgo[i] = (uint32_t)(r * (int)p.k_ss + 8 * c) * 2u;
+        vgo[i] = (uint32_t)(r * (int)p.v_ss + 8 * c) * 2u;
+    }
+    auto load_tile = [&](int kt, unsigned char *kdst, unsigned char *vdst) {
+        const int k0 = kt * BN;
+        if (k0 + BN <= p.Skv) {
+            const char *kb = (const char *)(kg + (int64_t)k0 * p.k_ss);
+            const char *vb = (const char *)(vg + (int64_t)k0 * p.v_ss);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                __builtin_amdgcn_global_load_lds((const void *)(kb + kgo[i]),
+                                                 (MM_LDS void *)(kdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vb + vgo[i]),
+                                                 (MM_LDS void *)(vdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int gr = min(k0 + trow[i], p.Skv - 1);
+                __builtin_amdgcn_global_load_lds((const void *)(kg + (int64_t)gr * p.k_ss + 8 * tchunk[i]),
+                                                 (MM_LDS void *)(kdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vg + (int64_t)gr * p.v_ss + 8 * tchunk[i]),
+                                                 (MM_LDS void *)(vdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
+            }
         }
     };
 
@@ -172,13 +217,10 @@ void fwd_mfma_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    if (kt_lo < kt_hi) load_tile(kt_lo, 0);
-    __syncthreads();
-
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int buf = (kt - kt_lo) & 1;
-        if (kt + 1 < kt_hi) load_tile(kt + 1, buf ^ 1);
-
+    // one tile: DMA the next tile into (Kn, Vn) while computing on (Kt, Vt)
+    auto tile = [&](int kt, const unsigned char *Kt, const unsigned char *Vt, unsigned char *Kn,
+                    unsigned char *Vn) {
+        if (kt + 1 < kt_hi) load_tile(kt + 1, Kn, Vn);
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
         bool skip = false, need_mask = k0 + BN > p.Skv;
@@ -192,9 +234,8 @@ void fwd_mfma_kernel(FwdParams p) {
         }
 
         if (!skip) {
-            const unsigned char *Kt = smem[buf][0];
-            const unsigned char *Vt = smem[buf][1];
             f32x16 sacc[NKB];
+            MM_PRIO_HI();
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 sacc[kb] = f32x16{};
@@ -204,9 +245,12 @@ void fwd_mfma_kernel(FwdParams p) {
                     sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
                 }
             }
-            // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4
-            float mloc = -INFINITY;
-            // general: alibi, masking or a non-positive scale; plain: max of raw dots * scale
+            MM_PRIO_LO();
+            // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4.
+            // general tiles (alibi, masking, non-positive scale) store t in sacc and use
+            // cc = 1; plain tiles keep the raw dot products and fold the scale into the
+            // exponent (cc = scale*log2e > 0 commutes with the max).
+            float mloc = -INFINITY, cc;
             const bool general = ALIBI || need_mask || !(c2 > 0.f);
             if (general) {
                 const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
@@ -227,15 +271,16 @@ void fwd_mfma_kernel(FwdParams p) {
                         mloc = fmaxf(mloc, t);
                     }
                 }
+                cc = 1.f;
             } else {
-                // scale > 0 commutes with the max
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
                 mloc *= c2;
+                cc = c2;
             }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+            mloc = row_max2(mloc);
             // lazy rescale: raise the running max only when the tile exceeds it by > 2^8
             if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescale)) {
                 const float m_new = fmaxf(m_run, mloc);
@@ -245,7 +290,7 @@ void fwd_mfma_kernel(FwdParams p) {
                 for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
                 m_run = m_new;
             }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            const float nm = m_run == -INFINITY ? 0.f : -m_run;
             // P = 2^(t - m) as 16-bit pairs; row sum from the same 16-bit values
             uint32_t pp[NKB][8];
             float psum = 0.f;
@@ -253,19 +298,14 @@ void fwd_mfma_kernel(FwdParams p) {
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int e2 = 0; e2 < 8; ++e2) {
-                    float x0, x1;
-                    if (general) {
-                        x0 = fast_exp2(sacc[kb][2 * e2] - m_use);
-                        x1 = fast_exp2(sacc[kb][2 * e2 + 1] - m_use);
-                    } else {
-                        x0 = fast_exp2(fmaf(sacc[kb][2 * e2], c2, -m_use));
-                        x1 = fast_exp2(fmaf(sacc[kb][2 * e2 + 1], c2, -m_use));
-                    }
+                    const float x0 = fast_exp2(fmaf(sacc[kb][2 * e2], cc, nm));
+                    const float x1 = fast_exp2(fmaf(sacc[kb][2 * e2 + 1], cc, nm));
                     pp[kb][e2] = pack2(x0, x1, TT{});
                     psum = dot2_ones(pp[kb][e2], psum, TT{});
                 }
             l_run += psum;
             // O^T += V^T P^T
+            MM_PRIO_HI();
 #pragma unroll
             for (int ks = 0; ks < BN / 16; ++ks) {
                 const int kb = ks >> 1, o4 = 4 * (ks & 1);
@@ -282,7 +322,17 @@ void fwd_mfma_kernel(FwdParams p) {
                 }
             }
         }
+    };
+
+    if (kt_lo < kt_hi) load_tile(kt_lo, kbuf0, vbuf0);
+    __syncthreads();
+    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+        tile(kt, kbuf0, vbuf0, kbuf1, vbuf1);
         __syncthreads();
+        if (kt + 1 < kt_hi) {
+            tile(kt + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue ----

@@ -131,9 +131,9 @@ def test_decode_rejects_before_launch(kw, status):
 
 
 def test_decode_workspace_and_splits():
-    # 1 x 32 heads x 64 splits x (128 + 2) floats
-    assert mm.decode_auto_splits(1, 32, 32768) == 64
-    assert mm.decode_workspace_size(1, 32, 32768, 128) == 32 * 64 * 130 * 4
+    # 1 x 32 heads x 32 splits x (128 + 2) floats
+    assert mm.decode_auto_splits(1, 32, 32768) == 32
+    assert mm.decode_workspace_size(1, 32, 32768, 128) == 32 * 32 * 130 * 4
     assert mm.decode_workspace_size(1, 32, 32768, 128, num_splits=3) == 32 * 3 * 130 * 4
     assert mm.decode_auto_splits(1, 32, 1) == 1
     assert mm.decode_auto_splits(1, 32, 0) == 1
