@@ -88,11 +88,11 @@ def cpu_baseline(x, target_s=10.0):
     scale = float(np.float32(1.0 / math.sqrt(D)))
     g = np.random.default_rng(123)
     threads = oracle.max_threads()
-    probe = g.integers(0, B * H * S, size=64)
+    probe = g.integers(0, B * H * S, size=4096)
     t0 = time.perf_counter()
     oracle.attention(qd, kd, vd, scale=scale, rows=probe)
     dt = max(time.perf_counter() - t0, 1e-6)
-    n = int(min(max(64 * target_s / dt, 64), 200000))
+    n = int(min(max(4096 * target_s / dt, 4096), 400000))
     rows = g.integers(0, B * H * S, size=n)
     t0 = time.perf_counter()
     oracle.attention(qd, kd, vd, scale=scale, rows=rows)
@@ -105,6 +105,67 @@ def cpu_baseline(x, target_s=10.0):
             "seconds": dt}
 
 
+COPY_BYTES = 1 << 30  # --only copy: 1 GiB read and 1 GiB written per call
+
+
+def _read_counters(path):
+    import csv
+    import collections
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+def _find(root, sub, suffix):
+    for dp, _, files in os.walk(os.path.join(root, sub)):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(dp, fn)
+    raise FileNotFoundError(f"{sub}/*{suffix} under {root}")
+
+
+def ingest(root):
+    """Turn rocprofv3 outputs under `root` into profiles/traffic.json and profiles/*.md.
+
+    Expects sub-directories fetch_{fwd,decode,copy} and write_{fwd,decode,copy} from
+    `rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --kernel-trace -f csv -- python bench.py --only X`
+    and `trace` from `rocprofv3 --kernel-trace --stats -f csv -- python bench.py`.
+    FETCH_SIZE / WRITE_SIZE are in KiB per dispatch; each is scaled by the factor that
+    maps the copy kernel's reading onto the bytes it really moves.
+    """
+    def per_dispatch(sub, counter, match):
+        data = _read_counters(_find(root, sub, "counter_collection.csv"))
+        vals = [v for k, cs in data.items() if match(k) for v in cs.get(counter, [])]
+        if not vals:
+            raise RuntimeError(f"no {counter} samples for {sub}")
+        return sum(vals) / len(vals) * 1024.0
+
+    is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower() and "mm::" not in k
+    f_copy = per_dispatch("fetch_copy", "FETCH_SIZE", is_copy)
+    w_copy = per_dispatch("write_copy", "WRITE_SIZE", is_copy)
+    kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    res = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_raw_bytes": f_copy, "write_raw_bytes": w_copy,
+                           "fetch_factor": round(kf, 4), "write_factor": round(kw, 4)}}
+    h = kernel_source_hash()
+    for name, sub, match, alg in [
+        (FWD_KERNEL, "fwd", lambda k: FWD_KERNEL in k, fwd_bytes(FWD["B"], FWD["H"], FWD["S"], FWD["D"])),
+        ("decode", "decode", lambda k: "decode_" in k, dec_bytes(DEC["B"], DEC["H"], DEC["L"], DEC["D"])),
+    ]:
+        fr = _read_counters(_find(root, "fetch_" + sub, "counter_collection.csv"))
+        wr = _read_counters(_find(root, "write_" + sub, "counter_collection.csv"))
+        fb = sum(sum(cs["FETCH_SIZE"]) / len(cs["FETCH_SIZE"]) for k, cs in fr.items() if match(k)) * 1024 * kf
+        wb = sum(sum(cs["WRITE_SIZE"]) / len(cs["WRITE_SIZE"]) for k, cs in wr.items() if match(k)) * 1024 * kw
+        res[name] = {"src_hash": h, "fetch_bytes": round(fb), "write_bytes": round(wb),
+                     "bytes_per_launch": round(fb + wb), "algorithmic_bytes": alg,
+                     "ratio_to_algorithmic": round((fb + wb) / alg, 3)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def profile_one(args, torch, mm, inputs, dev):
     """Run one kernel family only (for rocprofv3 passes); prints a small JSON line."""
     def dev_tensor(bits, dtype):
@@ -112,7 +173,7 @@ def profile_one(args, torch, mm, inputs, dev):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tt).to(dev)
 
     if args.only == "copy":
-        n = 1 << 29  # 2^29 fp16 = 1 GiB read + 1 GiB written per copy
+        n = COPY_BYTES // 2  # fp16 elements: 1 GiB read + 1 GiB written per copy
         src = torch.ones(n, dtype=torch.float16, device=dev)
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)
@@ -155,11 +216,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
                     help="profiling aid: run just one kernel family (or a plain 1 GiB device copy "
                          "used to calibrate the HBM byte counters) and print its timing")
+    ap.add_argument("--ingest", metavar="DIR", default=None,
+                    help="host only: turn rocprofv3 PMC outputs under DIR into profiles/traffic.json")
     args = ap.parse_args()
+    if args.ingest:
+        return ingest(args.ingest)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the attention shards by (batch, head) with no exchange; see the design notes).",
