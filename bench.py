@@ -216,7 +216,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
                     help="profiling aid: run just one kernel family (or a plain 1 GiB device copy "
                          "used to calibrate the HBM byte counters) and print its timing")

@@ -133,8 +133,7 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
         p.n_qtiles = 1;
         e = launch_fwd_f32(p, a->D, alibi, mask, s);
     } else {
-        p.n_qtiles = (a->Sq + kFwdBM - 1) / kFwdBM;
-        if ((int64_t)p.n_qtiles * a->Hq * a->B > 0x7fffffff) return MM_ERR_SHAPE;
+        if ((int64_t)((a->Sq + kFwdBM - 1) / kFwdBM) * a->Hq * a->B > 0x7fffffff) return MM_ERR_SHAPE;
         if (a->dtype == MM_BF16)
             e = a->D == 64 ? launch_fwd_mfma_bf16_d64(p, alibi, mask, s) : launch_fwd_mfma_bf16_d128(p, alibi, mask, s);
         else

@@ -1,9 +1,11 @@
 // fwd_mfma.h -- flash-attention forward for gfx950 with flex mods (bf16 / f16 inputs).
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, query head); each wave owns
-// 32 rows, two workgroups share a CU. Keys/values stream through LDS in tiles of 64
-// keys, double buffered: the next tile is copied global -> LDS by the DMA path
-// (global_load_lds_dwordx4, no VGPR staging) while the current tile is computed.
+// One workgroup = NW waves = 32*NW query rows of one (batch, query head); each wave owns
+// 32 rows. The default is 8 waves (256 rows, one workgroup per CU, two waves per SIMD):
+// every K/V tile copied into LDS then serves 256 rows, which halves the L2 -> LDS
+// traffic of a 4-wave layout. Keys/values stream through LDS in tiles of 64 keys in an
+// NST-stage ring (default 2): the tile NST-1 ahead is copied global -> LDS by the DMA
+// path (global_load_lds_dwordx4, no VGPR staging) while the current tile is computed.
 //
 // Both products run on the 32x32x16 MFMA with fp32 accumulation, in transposed form
 // so that a lane always owns one query row:
@@ -80,26 +82,65 @@ struct Tile {
     __host__ __device__ static constexpr int off(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
 };
 
-template <typename TT, int D, bool ALIBI, int MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4). The LDS destination
+// is M0 + 16*lane. Written in asm so the compiler does not track the copy: it would
+// otherwise wait for every copy in flight before reading any LDS buffer it cannot
+// prove disjoint. The kernel orders copies and reads itself (kv_barrier). No output
+// registers; the kernels leave nothing of their own in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is written on purpose (see above)
+__device__ __forceinline__ void dma16_sbase(const void *gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 ::"v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_vaddr(const void *gaddr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 ::"v"(gaddr), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const MM_LDS void *)p;
+}
+
+// barrier for the K/V pipeline: waits until this wave has at most VMCNT copies in
+// flight (older copies have landed: the vector-memory counter retires in order) and
+// its LDS reads are done, then synchronises the workgroup.
+template <int VMCNT>
+__device__ __forceinline__ void kv_barrier() {
+    static_assert(VMCNT >= 0 && VMCNT < 64, "vmcnt");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((VMCNT & 15) | ((VMCNT >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+template <typename TT, int D, bool ALIBI, int MASK, int NW, int NST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
-    constexpr int BM = kFwdBM, BN = 64;
+    constexpr int BM = 32 * NW, BN = 64;
     constexpr int KS = D / 16;    // k-steps of Q K^T
     constexpr int DB = D / 32;    // 32-row blocks of O^T
     constexpr int NKB = BN / 32;  // 32-key blocks of S^T per tile
     typedef Tile<D> TL;
     constexpr int TILEB = BN * TL::ROWB;            // bytes of one K (or V) tile
-    constexpr int LOADS = TILEB / 1024 / 4;         // DMA instructions per wave per tile
+    constexpr int LOADS = TILEB / 1024 / NW;        // DMA instructions per wave per tile
     constexpr int RPI = 1024 / TL::ROWB;            // rows per DMA instruction
     constexpr float kRescale = 8.f;                 // lazy-rescale threshold (log2 units)
     typedef typename TT::vec8 V8;
-    static_assert(LOADS >= 1, "tile shape");
+    static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
+    static_assert(NST == 2 || NST == 3, "stages");
 
-    // two K/V buffers as distinct LDS objects: the loop below is unrolled by two so each
-    // half reads one buffer while the DMA fills the other, and the compiler can see the
-    // reads never alias the in-flight copies (no early vmcnt wait).
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TILEB], vbuf0[TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[TILEB], vbuf1[TILEB];
+    // NST K/V buffers as distinct LDS objects: the loop below is unrolled by NST so every
+    // tile reads a statically known buffer while the DMA fills another, and the compiler
+    // can see the reads never alias the in-flight copies (no early vmcnt wait).
+    // (one object per stage, K then V: the waitcnt pass tracks only a few DMA targets)
+    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv2[NST > 2 ? 2 * TILEB : 16];
+    unsigned char *const KB[3] = {kv0, kv1, kv2};
+    unsigned char *const VB[3] = {kv0 + TILEB, kv1 + TILEB, kv2 + (NST > 2 ? TILEB : 0)};
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -190,24 +231,22 @@ void fwd_mfma_kernel(FwdParams p) {
     }
     auto load_tile = [&](int kt, unsigned char *kdst, unsigned char *vdst) {
         const int k0 = kt * BN;
+        const uint32_t kl = lds_addr(kdst) + (uint32_t)(wave_s * LOADS) * 1024u;
+        const uint32_t vl = lds_addr(vdst) + (uint32_t)(wave_s * LOADS) * 1024u;
         if (k0 + BN <= p.Skv) {
             const char *kb = (const char *)(kg + (int64_t)k0 * p.k_ss);
             const char *vb = (const char *)(vg + (int64_t)k0 * p.v_ss);
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
-                __builtin_amdgcn_global_load_lds((const void *)(kb + kgo[i]),
-                                                 (MM_LDS void *)(kdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vb + vgo[i]),
-                                                 (MM_LDS void *)(vdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
+                dma16_sbase(kb, kgo[i], kl + i * 1024);
+                dma16_sbase(vb, vgo[i], vl + i * 1024);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 const int gr = min(k0 + trow[i], p.Skv - 1);
-                __builtin_amdgcn_global_load_lds((const void *)(kg + (int64_t)gr * p.k_ss + 8 * tchunk[i]),
-                                                 (MM_LDS void *)(kdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vg + (int64_t)gr * p.v_ss + 8 * tchunk[i]),
-                                                 (MM_LDS void *)(vdst + (wave_s * LOADS + i) * 1024), 16, 0, 0);
+                dma16_vaddr(kg + (int64_t)gr * p.k_ss + 8 * tchunk[i], kl + i * 1024);
+                dma16_vaddr(vg + (int64_t)gr * p.v_ss + 8 * tchunk[i], vl + i * 1024);
             }
         }
     };
@@ -217,13 +256,16 @@ void fwd_mfma_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // one tile: DMA the next tile into (Kn, Vn) while computing on (Kt, Vt)
+    // one tile: DMA the tile NST-1 ahead into (Kn, Vn) while computing on (Kt, Vt)
     auto tile = [&](int kt, const unsigned char *Kt, const unsigned char *Vt, unsigned char *Kn,
                     unsigned char *Vn) {
-        if (kt + 1 < kt_hi) load_tile(kt + 1, Kn, Vn);
+        // always copy (past the end: the last tile again, into a buffer nobody reads),
+        // so every tile issues the same DMA and the pipeline waits are uniform
+        if (NST > 2) load_tile(min(kt + NST - 1, kt_hi - 1), Kn, Vn);
+        else if (kt + 1 < kt_hi) load_tile(kt + 1, Kn, Vn);
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
-        bool skip = false, need_mask = k0 + BN > p.Skv;
+        bool skip = kt >= kt_hi, need_mask = k0 + BN > p.Skv;
         if (MASK & MASK_CAUSAL) {
             skip |= k0 > r_last;
             need_mask |= k0 + BN - 1 > r0;
@@ -236,14 +278,23 @@ void fwd_mfma_kernel(FwdParams p) {
         if (!skip) {
             f32x16 sacc[NKB];
             MM_PRIO_HI();
+            {
+                // all K fragments first, then the MFMAs: the reads overlap each other
+                // instead of each MFMA waiting on its own read
+                u32x4 ka[NKB][KS];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                sacc[kb] = f32x16{};
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const V8 a = as_vec<V8>(*(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[ks]));
-                    sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
+                    for (int ks = 0; ks < KS; ++ks)
+                        ka[kb][ks] = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[ks]);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    sacc[kb] = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) sacc[kb] = mfma32x32x16(as_vec<V8>(ka[kb][ks]), qf[ks], sacc[kb]);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, NKB * KS, 0);  // DS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, NKB * KS, 0);  // then MFMAs
             }
             MM_PRIO_LO();
             // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4.
@@ -304,36 +355,56 @@ void fwd_mfma_kernel(FwdParams p) {
                     psum = dot2_ones(pp[kb][e2], psum, TT{});
                 }
             l_run += psum;
-            // O^T += V^T P^T
+            // O^T += V^T P^T (all transposed V reads first, then the MFMAs)
             MM_PRIO_HI();
+            {
+                u32x4 va[BN / 16][DB];
 #pragma unroll
-            for (int ks = 0; ks < BN / 16; ++ks) {
-                const int kb = ks >> 1, o4 = 4 * (ks & 1);
-                const V8 pf = as_vec<V8>(u32x4{pp[kb][o4], pp[kb][o4 + 1], pp[kb][o4 + 2], pp[kb][o4 + 3]});
+                for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][0]));
-                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][1]));
-                    const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi4);
-                    const V8 a = as_vec<V8>(u32x4{a0[0], a0[1], a1[0], a1[1]});
-                    oacc[db] = mfma32x32x16(a, pf, oacc[db]);
+                    for (int db = 0; db < DB; ++db) {
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][0]));
+                        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][1]));
+                        const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi4);
+                        va[ks][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    }
+#pragma unroll
+                for (int ks = 0; ks < BN / 16; ++ks) {
+                    const int kb = ks >> 1, o4 = 4 * (ks & 1);
+                    const V8 pf = as_vec<V8>(u32x4{pp[kb][o4], pp[kb][o4 + 1], pp[kb][o4 + 2], pp[kb][o4 + 3]});
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(as_vec<V8>(va[ks][db]), pf, oacc[db]);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (BN / 16) * DB, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, (BN / 16) * DB, 1);
             }
         }
     };
 
-    if (kt_lo < kt_hi) load_tile(kt_lo, kbuf0, vbuf0);
-    __syncthreads();
-    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-        tile(kt, kbuf0, vbuf0, kbuf1, vbuf1);
-        __syncthreads();
-        if (kt + 1 < kt_hi) {
-            tile(kt + 1, kbuf1, vbuf1, kbuf0, vbuf0);
-            __syncthreads();
+    if (kt_lo < kt_hi) {
+#pragma unroll
+        for (int st = 0; st < NST - 1; ++st) load_tile(min(kt_lo + st, kt_hi - 1), KB[st], VB[st]);
+    }
+    kv_barrier<0>();
+    for (int kt = kt_lo; kt < kt_hi; kt += NST) {
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            if (NST == 2) {
+                if (kt + st < kt_hi) {
+                    tile(kt + st, KB[st], VB[st], KB[(st + 1) % NST], VB[(st + 1) % NST]);
+                    kv_barrier<0>();
+                }
+            } else {
+                // three stages: the copies issued during this tile stay in flight; the
+                // ones issued a tile earlier (the next tile's) must have landed
+                tile(kt + st, KB[st], VB[st], KB[(st + NST - 1) % NST], VB[(st + NST - 1) % NST]);
+                kv_barrier<2 * LOADS>();
+            }
         }
     }
+    if (NST > 2) kv_barrier<0>();  // drain the copies issued past the end
 
     // ---- epilogue ----
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -361,23 +432,40 @@ void fwd_mfma_kernel(FwdParams p) {
     }
 }
 
+#ifndef MM_FWD_NW
+#define MM_FWD_NW 8  // waves per workgroup without a mask mod
+#endif
+#ifndef MM_FWD_NW_MASKED
+#define MM_FWD_NW_MASKED 4  // with causal / window masks: finer row tiles skip more keys
+#endif
+#ifndef MM_FWD_NST
+#define MM_FWD_NST 2
+#endif
+
+template <typename TT, int D, bool A, int M>
+hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
+    // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic; with
+    // causal or window masks, 4-wave tiles (128 rows) follow the diagonal / band more
+    // closely and skip more key tiles, which matters more
+    constexpr int NW = M == 0 ? MM_FWD_NW : MM_FWD_NW_MASKED, NST = MM_FWD_NST;
+    p.n_qtiles = (p.Sq + 32 * NW - 1) / (32 * NW);
+    const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(64 * NW);
+    fwd_mfma_kernel<TT, D, A, M, NW, NST><<<grid, block, 0, s>>>(p);
+    return hipGetLastError();
+}
+
 template <typename TT, int D>
 hipError_t launch_fwd_mfma(const FwdParams &p, bool alibi, int mask, hipStream_t s) {
-    const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(256);
-#define MM_FWD_CASE(A, M) \
-    case (A) * 4 + (M): fwd_mfma_kernel<TT, D, (A) != 0, (M)><<<grid, block, 0, s>>>(p); break;
     switch ((alibi ? 4 : 0) + (mask & 3)) {
-        MM_FWD_CASE(0, 0)
-        MM_FWD_CASE(0, 1)
-        MM_FWD_CASE(0, 2)
-        MM_FWD_CASE(0, 3)
-        MM_FWD_CASE(1, 0)
-        MM_FWD_CASE(1, 1)
-        MM_FWD_CASE(1, 2)
-        MM_FWD_CASE(1, 3)
+        case 0: return launch_fwd_mfma_one<TT, D, false, 0>(p, s);
+        case 1: return launch_fwd_mfma_one<TT, D, false, 1>(p, s);
+        case 2: return launch_fwd_mfma_one<TT, D, false, 2>(p, s);
+        case 3: return launch_fwd_mfma_one<TT, D, false, 3>(p, s);
+        case 4: return launch_fwd_mfma_one<TT, D, true, 0>(p, s);
+        case 5: return launch_fwd_mfma_one<TT, D, true, 1>(p, s);
+        case 6: return launch_fwd_mfma_one<TT, D, true, 2>(p, s);
+        default: return launch_fwd_mfma_one<TT, D, true, 3>(p, s);
     }
-#undef MM_FWD_CASE
-    return hipGetLastError();
 }
 
 }  // namespace mm
