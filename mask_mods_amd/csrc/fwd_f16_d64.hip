@@ -1,12 +1,8 @@
 // Forward MFMA kernel instantiations: f16 inputs, head dim 64.
-#include "fwd_pingpong.h"
+#include "fwd_mfma.h"
 
 namespace mm {
 hipError_t launch_fwd_mfma_f16_d64(const FwdParams &p, bool alibi, int mask, hipStream_t s) {
-    #if MM_FWD_PP
-    return launch_fwd_pp<F16, 64>(p, alibi, mask, s);
-#else
     return launch_fwd_mfma<F16, 64>(p, alibi, mask, s);
-#endif
 }
 }  // namespace mm

@@ -41,12 +41,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 #define MM_LDS __attribute__((address_space(3)))
-#ifndef MM_SETPRIO
-#define MM_SETPRIO 0
-#endif
-// wave priority while issuing MFMA blocks (helps the two waves of a SIMD alternate)
-#define MM_PRIO_HI() do { if (MM_SETPRIO) __builtin_amdgcn_s_setprio(1); } while (0)
-#define MM_PRIO_LO() do { if (MM_SETPRIO) __builtin_amdgcn_s_setprio(0); } while (0)
 
 // row sum helper: acc + p.x + p.y on the 16-bit pair that feeds the PV MFMA
 __device__ __forceinline__ float dot2_ones(uint32_t pair, float acc, BF16) {
@@ -277,7 +271,6 @@ void fwd_mfma_kernel(FwdParams p) {
 
         if (!skip) {
             f32x16 sacc[NKB];
-            MM_PRIO_HI();
             {
                 // all K fragments first, then the MFMAs: the reads overlap each other
                 // instead of each MFMA waiting on its own read
@@ -296,7 +289,6 @@ void fwd_mfma_kernel(FwdParams p) {
                 __builtin_amdgcn_sched_group_barrier(0x100, NKB * KS, 0);  // DS reads
                 __builtin_amdgcn_sched_group_barrier(0x008, NKB * KS, 0);  // then MFMAs
             }
-            MM_PRIO_LO();
             // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4.
             // general tiles (alibi, masking, non-positive scale) store t in sacc and use
             // cc = 1; plain tiles keep the raw dot products and fold the scale into the
@@ -356,7 +348,6 @@ void fwd_mfma_kernel(FwdParams p) {
                 }
             l_run += psum;
             // O^T += V^T P^T (all transposed V reads first, then the MFMAs)
-            MM_PRIO_HI();
             {
                 u32x4 va[BN / 16][DB];
 #pragma unroll

@@ -47,9 +47,6 @@ struct DecParams {
 
 // Smallest number of query rows per forward workgroup (host-side grid bound).
 constexpr int kFwdBM = 128;
-#ifndef MM_FWD_PP
-#define MM_FWD_PP 0
-#endif
 
 // dtype: 1 = f16, 2 = bf16 (the mm_dtype values)
 hipError_t launch_fwd_mfma_bf16_d64(const FwdParams &p, bool alibi, int mask, hipStream_t s);
