@@ -133,3 +133,20 @@ def test_deterministic():
     o2, l2 = mm.attn_decode(q, k, v, 8000, SCALE, mask=m)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_workspace_reuse_across_calls_and_split_counts():
+    """One workspace serves many calls with different split counts."""
+    import torch
+    import mask_mods_amd as mm
+    x = inputs.decode_inputs(12, 2, 16, 16, [3000, 1200], 128, "f16")
+    q, k, v = (to_torch(x[n], "f16") for n in ("q", "k", "v"))
+    m = to_torch(x["mask"], "f16")
+    seq = torch.tensor(x["lens"], dtype=torch.int32, device="cuda")
+    ws = torch.empty(mm.decode_workspace_size(2, 16, 3000, 128, num_splits=64) // 4 + 4,
+                     dtype=torch.float32, device="cuda")
+    ref, lref = mm.attn_decode(q, k, v, 3000, SCALE, mask=m, seq_lens=seq)
+    for splits in (64, 3, 17, 1, 64, 40):
+        o, l = mm.attn_decode(q, k, v, 3000, SCALE, mask=m, seq_lens=seq, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.allclose(o.float(), ref.float(), atol=2e-3) and torch.allclose(l, lref, atol=1e-5)
