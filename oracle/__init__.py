@@ -23,6 +23,8 @@ _lib = None
 _dp = ctypes.POINTER(ctypes.c_double)
 _ip = ctypes.POINTER(ctypes.c_int32)
 _lp = ctypes.POINTER(ctypes.c_int64)
+_bp = ctypes.POINTER(ctypes.c_uint8)
+BLOCK_Q, BLOCK_KV = 128, 64  # block-mask granularity (query rows x keys)
 
 
 def build() -> str:
@@ -58,6 +60,7 @@ def load():
         ctypes.c_double, ctypes.c_int, _dp,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
         _dp, ctypes.c_int64, _ip,
+        _bp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         _lp, ctypes.c_int64, _dp, _dp,
     ]
     lib.oracle_attention.restype = ctypes.c_int
@@ -90,7 +93,7 @@ def _ptr(a, typ):
 
 
 def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=False,
-              slopes=None, rowdrop=None, add_mask=None, lens=None, rows=None):
+              slopes=None, rowdrop=None, add_mask=None, lens=None, rows=None, block_mask=None):
     """Run the oracle.
 
     q: float64 [B,Hq,Sq,D]; k, v: float64 [B,Hkv,kv_cap,D] (first ``Skv`` keys used,
@@ -98,6 +101,8 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
     add_mask: None or float64 [B,Hq,Sq,mask_ld]. lens: None or int [B].
     rows: None (all rows; returns O [B,Hq,Sq,D], LSE [B,Hq,Sq]) or flat row ids
     (b*Hq + h)*Sq + i (returns O [n,D], LSE [n]).
+    block_mask: None or uint8 [B or 1, Hq or 1, ceil(Sq/128), ceil(Skv/64)] with
+    0 = block masked, 1 = predicates decide, 2 = block kept (size-1 dims broadcast).
     """
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -125,12 +130,20 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
     out = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
     seed, thr = (0, 0) if rowdrop is None else rowdrop
+    bm_s = (0, 0, 0)
+    if block_mask is not None:
+        block_mask = np.ascontiguousarray(block_mask, dtype=np.uint8)
+        Bb, Hb, nqb, nkb = block_mask.shape
+        assert Bb in (1, B) and Hb in (1, Hq)
+        assert nqb >= -(-Sq // BLOCK_Q) and nkb >= -(-Skv // BLOCK_KV)
+        bm_s = (0 if Bb == 1 else Hb * nqb * nkb, 0 if Hb == 1 else nqb * nkb, nkb)
     rc = load().oracle_attention(
         B, Hq, Hkv, Sq, Skv, D, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), kv_cap,
         float(scale), int(bool(alibi)), _ptr(slopes, _dp),
         int(bool(causal)), -1 if window is None else int(window), int(rowdrop is not None),
         seed & 0xFFFFFFFF, thr & 0xFFFFFFFF,
         _ptr(add_mask, _dp), mask_ld, _ptr(lens, _ip),
+        _ptr(block_mask, _bp), bm_s[0], bm_s[1], bm_s[2],
         _ptr(rows, _lp), n if rows is not None else 0, _ptr(out, _dp), _ptr(lse, _dp))
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")

@@ -33,6 +33,13 @@
  *                    Austin Appleby's MurmurHash3 (public domain).
  * alibi slope for query head h of H: 2^(-8(h+1)/H) unless slopes are given.
  *
+ * Block mask (optional, BlockMask-style): one byte per (b, h, q block of 128 rows,
+ * kv block of 64 keys): 0 = no pair of the block is kept; 2 = every pair is kept and
+ * the mask_mod predicates (causal, window) are not evaluated there; 1 = the predicates
+ * decide. The row-drop mod and the key-length bound apply everywhere. This is the
+ * FlyDSL PR's named future phase (block sparsity), read as PyTorch's BlockMask with
+ * its full / partial block lists.
+ *
  * Inputs are float64 arrays holding the exact values of the bf16/f16/f32 inputs.
  * Nothing here is blocked, fused, reordered or rounded beyond that definition.
  */
@@ -93,7 +100,12 @@ typedef struct {
     const double *add_mask;
     int64_t mask_ld;
     const int32_t *lens;
+    const uint8_t *block_mask;
+    int64_t bm_sb, bm_sh, bm_sq;
 } problem;
+
+#define ORACLE_BLOCK_Q 128
+#define ORACLE_BLOCK_KV 64
 
 /* One query row. s: scratch of Skv doubles. o: D outputs. */
 static void attend_row(const problem *p, int b, int h, int i, double *s, double *o, double *lse)
@@ -111,8 +123,15 @@ static void attend_row(const problem *p, int b, int h, int i, double *s, double 
     double M = -INFINITY;
     for (int j = 0; j < p->Skv; ++j) {
         int keep = !dropped && j < len;
-        if (p->causal && !(j <= i)) keep = 0;
-        if (p->window >= 0 && !(abs(i - j) <= p->window)) keep = 0;
+        int blk = 1;
+        if (p->block_mask)
+            blk = p->block_mask[b * p->bm_sb + h * p->bm_sh + (int64_t)(i / ORACLE_BLOCK_Q) * p->bm_sq +
+                                j / ORACLE_BLOCK_KV];
+        if (blk == 0) keep = 0;
+        if (blk == 1) {
+            if (p->causal && !(j <= i)) keep = 0;
+            if (p->window >= 0 && !(abs(i - j) <= p->window)) keep = 0;
+        }
         if (!keep) {
             s[j] = -INFINITY;
             continue;
@@ -148,6 +167,7 @@ static void attend_row(const problem *p, int b, int h, int i, double *s, double 
  *   window < 0 disables the sliding window
  *   add_mask: NULL or additive bias, element (row, j) at add_mask[row*mask_ld + j]
  *   lens:  NULL or per-batch key count (keys j >= lens[b] are masked)
+ *   block_mask: NULL or bytes indexed b*bm_sb + h*bm_sh + (i/128)*bm_sq + j/64
  *   rows:  NULL -> every row in order; else nrows flat row ids (b*Hq + h)*Sq + i
  *   out [nrows, D], lse [nrows]
  */
@@ -156,6 +176,7 @@ int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                      double scale, int alibi, const double *slopes,
                      int causal, int window, int rowdrop, uint32_t seed, uint32_t threshold,
                      const double *add_mask, int64_t mask_ld, const int32_t *lens,
+                     const uint8_t *block_mask, int64_t bm_sb, int64_t bm_sh, int64_t bm_sq,
                      const int64_t *rows, int64_t nrows, double *out, double *lse)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return -1;
@@ -164,7 +185,8 @@ int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
     const int64_t total = (int64_t)B * Hq * Sq;
     if (!rows) nrows = total;
     problem p = {B, Hq, Hkv, Sq, Skv, D, kv_cap, q, k, v, scale, alibi, slopes,
-                 causal, window, rowdrop, seed, threshold, add_mask, mask_ld, lens};
+                 causal, window, rowdrop, seed, threshold, add_mask, mask_ld, lens,
+                 block_mask, bm_sb, bm_sh, bm_sq};
     int bad = 0;
 #pragma omp parallel
     {

@@ -412,3 +412,82 @@ def test_fully_masked_rows_zero_and_neg_inf():
     assert np.all(L == -np.inf) and np.all(O == 0)
     O, L = oracle.attention(q, k, v, scale=0.4, rowdrop=(1, 0xFFFFFFFF))
     assert np.all(L == -np.inf) and np.all(O == 0)
+
+
+# ------------------------------------------------------------- block masks
+def _expand_block_mask(bm, B, Hq, Sq, Skv, causal, window):
+    """Element keep-mask from a block mask: 0 drops, 2 keeps, 1 defers to the predicates."""
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Skv)[None, :]
+    pred = np.ones((Sq, Skv), dtype=bool)
+    if causal:
+        pred &= j <= i
+    if window is not None:
+        pred &= np.abs(i - j) <= window
+    blk = np.broadcast_to(bm, (B, Hq) + bm.shape[2:])[:, :, i // oracle.BLOCK_Q, j // oracle.BLOCK_KV]
+    return (blk == 2) | ((blk == 1) & pred[None, None])
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 40), (False, 70)])
+def test_block_mask_vs_brute_force(causal, window):
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 300, 200, 8
+    x = inputs.attention_inputs(21, B, Hq, Hkv, Sq, Skv, D, "f32")
+    q, k, v = (_f64(x[n], "f32") for n in ("q", "k", "v"))
+    g = np.random.default_rng(22)
+    bm = g.integers(0, 3, size=(B, 1, 3, 4)).astype(np.uint8)  # broadcast over heads
+    bm[0, 0, 1, :] = 0                                            # a fully masked block row
+    O, L = oracle.attention(q, k, v, scale=0.3, causal=causal, window=window, block_mask=bm)
+    keep = _expand_block_mask(bm, B, Hq, Sq, Skv, causal, window)
+    kk, vv = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    S = np.where(keep, 0.3 * np.matmul(q, np.swapaxes(kk, -1, -2)), -np.inf)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        Lb = logsumexp(S, axis=-1)
+        P = np.where(np.isfinite(Lb)[..., None], np.exp(S - Lb[..., None]), 0.0)
+    close(O, np.matmul(P, vv), 1e-11)
+    close(L, Lb, 1e-11)
+    assert np.all(L[0, :, 128:256] == -np.inf)
+
+
+def test_block_mask_invariants():
+    B, H, S, D = 1, 2, 260, 8
+    q, k, v = _rand(B, H, H, S, S, D, seed=5)
+    nq, nk = -(-S // 128), -(-S // 64)
+    # full blocks skip the predicates: all-2 with causal == no mask at all
+    O0, L0 = oracle.attention(q, k, v, scale=0.4)
+    O1, L1 = oracle.attention(q, k, v, scale=0.4, causal=True, block_mask=np.full((1, 1, nq, nk), 2, np.uint8))
+    np.testing.assert_array_equal(O0, O1)
+    np.testing.assert_array_equal(L0, L1)
+    # all-1 with causal == causal
+    Oc, Lc = oracle.attention(q, k, v, scale=0.4, causal=True)
+    O2, L2 = oracle.attention(q, k, v, scale=0.4, causal=True, block_mask=np.ones((1, 1, nq, nk), np.uint8))
+    np.testing.assert_array_equal(Oc, O2)
+    np.testing.assert_array_equal(Lc, L2)
+    # causal block classes (empty above, full below, partial on the diagonal) == causal
+    qb = np.arange(nq)[:, None]
+    kb = np.arange(nk)[None, :]
+    lo_k, hi_k = kb * 64, kb * 64 + 63
+    lo_q, hi_q = qb * 128, np.minimum(qb * 128 + 127, S - 1)
+    cls = np.where(lo_k > hi_q, 0, np.where(hi_k <= lo_q, 2, 1)).astype(np.uint8)[None, None]
+    O3, L3 = oracle.attention(q, k, v, scale=0.4, causal=True, block_mask=cls)
+    np.testing.assert_array_equal(Oc, O3)
+    np.testing.assert_array_equal(Lc, L3)
+    # everything dropped
+    O4, L4 = oracle.attention(q, k, v, scale=0.4, block_mask=np.zeros((1, 1, nq, nk), np.uint8))
+    assert np.all(O4 == 0) and np.all(L4 == -np.inf)
+
+
+def test_block_mask_closed_form_counts():
+    """Q = 0: every kept key scores 0, so LSE = ln(number of kept keys) per row."""
+    S = 200
+    q, k, v = _zero_q(1, 1, 1, S, S, 4)
+    bm = np.array([[[[2, 0, 1, 2], [0, 1, 2, 1]]]], dtype=np.uint8)
+    _, L = oracle.attention(q, k, v, scale=1.0, causal=True, block_mask=bm)
+    for i in range(S):
+        n = 0
+        for j in range(S):
+            c = bm[0, 0, i // 128, j // 64]
+            n += c == 2 or (c == 1 and j <= i)
+        if n == 0:
+            assert L[0, 0, i] == -np.inf
+        else:
+            assert L[0, 0, i] == pytest.approx(math.log(n), abs=1e-14)

@@ -31,6 +31,9 @@ MUTANTS = {
     "fmix_constant": ("0x85ebca6bu", "0x85ebca6cu"),
     "drop_inverted": ("< threshold;", ">= threshold;"),
     "no_normalise": ("o[d] /= Lsum;", "o[d] /= 1.0;"),
+    "full_block_predicated": ("if (blk == 1) {", "if (blk != 0) {"),
+    "block_kv_size": ("j / ORACLE_BLOCK_KV];", "j / ORACLE_BLOCK_Q];"),
+    "block_empty_kept": ("if (blk == 0) keep = 0;", "if (blk == 3) keep = 0;"),
 }
 
 
