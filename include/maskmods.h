@@ -76,6 +76,22 @@ enum {
                              32-bit finalizer                                           */
 };
 
+/*
+ * Block mask (block sparsity, the phase FlyDSL PR #931 names as future work, in the
+ * shape of PyTorch's BlockMask with its full and partial block lists): one byte per
+ * (b, h, query block of MM_BLOCK_Q rows, key block of MM_BLOCK_KV keys):
+ *   0        no pair of the block is kept; its keys are never read,
+ *   1        partial: the mask_mod predicates (causal, window) decide per pair,
+ *   2        full: every pair is kept and the predicates are not evaluated.
+ * Other values are reserved and currently act as 2. MM_MASK_ROWDROP and the key-length
+ * bound apply in every block. Byte (b, h, qb, kb) sits at
+ *   block_mask[b*s[0] + h*s[1] + qb*s[2] + kb],  s = block_mask_strides,
+ * for qb < ceil(Sq/MM_BLOCK_Q), kb < ceil(Skv/MM_BLOCK_KV); a stride of 0 broadcasts
+ * that dimension. The table is a DEVICE pointer, borrowed like the tensors.
+ */
+#define MM_BLOCK_Q 128
+#define MM_BLOCK_KV 64
+
 typedef struct mm_mods {
     int32_t score_mod;            /* mm_score_mod                                      */
     uint32_t mask_flags;          /* OR of MM_MASK_*                                   */
@@ -83,6 +99,8 @@ typedef struct mm_mods {
     uint32_t rowdrop_seed;        /* MM_MASK_ROWDROP                                   */
     uint32_t rowdrop_threshold;   /* MM_MASK_ROWDROP: ~threshold/2^32 of rows dropped  */
     const float *alibi_slopes;    /* device fp32 [Hq], or NULL for 2^(-8(h+1)/Hq)      */
+    const uint8_t *block_mask;    /* device block mask (above), or NULL for none       */
+    int64_t block_mask_strides[3];/* elements (bytes), for b, h, query block; >= 0     */
 } mm_mods;
 
 typedef struct mm_fwd_args {
@@ -136,6 +154,19 @@ mm_status mm_attn_decode(const mm_decode_args *args, void *stream);
 
 /* Split count mm_attn_decode uses when num_splits == 0. */
 int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t kv_len);
+
+/* Block-mask classes of the built-in mask_mods, the analogue of building a BlockMask
+ * from a mask_mod: out[qb*ld + kb] (device bytes, qb < ceil(Sq/MM_BLOCK_Q),
+ * kb < ceil(Skv/MM_BLOCK_KV), ld >= ceil(Skv/MM_BLOCK_KV)) gets 0 if the predicates of
+ * `mask_flags` (MM_MASK_CAUSAL, MM_MASK_WINDOW with half-width `window`) keep no pair
+ * (q_idx < Sq, kv_idx < Skv) of the block, 2 if they keep every such pair, else 1.
+ * With no flag every block is 2. The table does not depend on b or h: pass it to
+ * mm_attn_fwd with block_mask_strides {0, 0, ld} and the same mask_flags, and the
+ * result equals that of the predicates alone, with empty blocks never read.
+ * MM_MASK_ROWDROP is rejected here (it is per row; mm_attn_fwd applies it anyway).
+ * One launch on `stream`; Sq or Skv of 0 writes nothing. */
+mm_status mm_block_mask_create(uint32_t mask_flags, int32_t window, int32_t Sq, int32_t Skv,
+                               uint8_t *out, int64_t ld, void *stream);
 
 /* Static string for a status code. */
 const char *mm_status_str(int32_t status);

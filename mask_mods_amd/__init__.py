@@ -17,10 +17,10 @@ import math
 import os
 
 __all__ = [
-    "attn_fwd", "attn_decode", "decode_workspace_size", "decode_auto_splits",
+    "attn_fwd", "attn_decode", "decode_workspace_size", "decode_auto_splits", "block_mask_create",
     "MaskModsError", "library_path", "load_library",
     "SCORE_NONE", "SCORE_ALIBI", "MASK_CAUSAL", "MASK_WINDOW", "MASK_ROWDROP",
-    "ROWDROP_5PCT",
+    "ROWDROP_5PCT", "BLOCK_Q", "BLOCK_KV", "BLOCK_EMPTY", "BLOCK_PARTIAL", "BLOCK_FULL",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,9 @@ MM_F32, MM_F16, MM_BF16 = 0, 1, 2
 SCORE_NONE, SCORE_ALIBI = 0, 1
 MASK_CAUSAL, MASK_WINDOW, MASK_ROWDROP = 1, 2, 4
 ROWDROP_5PCT = int(0.05 * 2 ** 32)  # threshold that drops ~5% of rows
+# block mask: query rows x keys per block, and the per-block classes
+BLOCK_Q, BLOCK_KV = 128, 64
+BLOCK_EMPTY, BLOCK_PARTIAL, BLOCK_FULL = 0, 1, 2
 
 _STATUS = {
     0: "MM_OK", -1: "MM_ERR_NULL", -2: "MM_ERR_SHAPE", -3: "MM_ERR_DTYPE",
@@ -52,6 +55,8 @@ class _Mods(ctypes.Structure):
         ("rowdrop_seed", ctypes.c_uint32),
         ("rowdrop_threshold", ctypes.c_uint32),
         ("alibi_slopes", ctypes.c_void_p),
+        ("block_mask", ctypes.c_void_p),
+        ("block_mask_strides", ctypes.c_int64 * 3),
     ]
 
 
@@ -114,6 +119,9 @@ def load_library():
     lib.mm_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.mm_attn_decode_auto_splits.argtypes = [ctypes.c_int32] * 3
     lib.mm_attn_decode_auto_splits.restype = ctypes.c_int32
+    lib.mm_block_mask_create.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.mm_block_mask_create.restype = ctypes.c_int32
     lib.mm_status_str.argtypes = [ctypes.c_int32]
     lib.mm_status_str.restype = ctypes.c_char_p
     lib.mm_fwd_args_size.restype = ctypes.c_size_t
@@ -156,24 +164,29 @@ def _check_dev(*ts):
             dev = t.device
         elif t.device != dev:
             raise ValueError("all tensors must be on the same device")
-        if t.dim() >= 1 and t.stride(-1) != 1 and t.size(-1) > 1:
+        if t.dim() >= 1 and t.stride(-1) != 1 and t.size(-1) > 1 and t.numel() > 0:
             raise ValueError("the last (head) dimension must be contiguous")
     return dev
 
 
 def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_slopes=None,
-             mask_flags=0, window=None, rowdrop=None, return_lse=True, out=None, lse=None):
+             mask_flags=0, window=None, rowdrop=None, block_mask=None, return_lse=True,
+             out=None, lse=None):
     """Fused attention forward.
 
     q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (bf16, f16 or f32; D in {64,128}).
     score_mod: SCORE_NONE or SCORE_ALIBI (or the string "alibi").
     mask_flags: OR of MASK_CAUSAL / MASK_WINDOW / MASK_ROWDROP; ``window`` sets
     MASK_WINDOW, ``rowdrop=(seed, threshold)`` sets MASK_ROWDROP.
+    block_mask: optional uint8 device tensor [B|1, Hq|1, >=ceil(Sq/128), >=ceil(Skv/64)],
+    one class per (query block of BLOCK_Q rows, key block of BLOCK_KV keys):
+    BLOCK_EMPTY (skipped), BLOCK_PARTIAL (the mask predicates decide) or BLOCK_FULL
+    (all kept); size-1 leading dims broadcast.
     Returns (out, lse) with lse fp32 [B,Hq,Sq] (None if return_lse is False).
     """
     torch = _torch()
     lib = load_library()
-    dev = _check_dev(q, k, v, out, lse, alibi_slopes)
+    dev = _check_dev(q, k, v, out, lse, alibi_slopes, block_mask)
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
     if v.shape != k.shape or Bk != B or Dk != D or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -200,6 +213,18 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
         if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (Hq,) \
                 or not alibi_slopes.is_contiguous():
             raise ValueError("alibi_slopes must be contiguous fp32 [Hq]")
+    bm_strides = (0, 0, 0)
+    if block_mask is not None:
+        nqb, nkb = -(-Sq // BLOCK_Q), -(-Skv // BLOCK_KV)
+        if block_mask.dtype != torch.uint8 or block_mask.dim() != 4:
+            raise ValueError("block_mask must be a 4-D uint8 tensor")
+        bb, bh, bq, bk = block_mask.shape
+        if bb not in (1, B) or bh not in (1, Hq) or bq < nqb or bk < nkb:
+            raise ValueError(f"block_mask shape {tuple(block_mask.shape)} does not cover "
+                             f"[{B}|1, {Hq}|1, {nqb}, {nkb}]")
+        if bk > 1 and block_mask.stride(3) != 1:
+            raise ValueError("block_mask's last dimension must be contiguous")
+        bm_strides = tuple(0 if n == 1 else st for n, st in zip(block_mask.shape[:3], block_mask.stride()[:3]))
     a = FwdArgs()
     a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
@@ -217,10 +242,36 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
     a.mods.rowdrop_seed = seed & 0xFFFFFFFF
     a.mods.rowdrop_threshold = thr & 0xFFFFFFFF
     a.mods.alibi_slopes = alibi_slopes.data_ptr() if alibi_slopes is not None else None
+    a.mods.block_mask = block_mask.data_ptr() if block_mask is not None and block_mask.numel() else None
+    a.mods.block_mask_strides = _I64x3(*bm_strides)
     st = lib.mm_attn_fwd(ctypes.byref(a), _stream_ptr(dev))
     if st != 0:
         raise MaskModsError(st, "mm_attn_fwd")
     return out, (lse if return_lse else None)
+
+
+def block_mask_create(Sq, Skv, *, causal=False, window=None, device=None, out=None):
+    """Block-mask classes of the built-in predicates, uint8 [1, 1, ceil(Sq/128), ceil(Skv/64)].
+
+    Pass the result to attn_fwd(block_mask=...) together with the same causal / window
+    arguments: empty blocks are then never read and full blocks skip the predicates.
+    """
+    torch = _torch()
+    lib = load_library()
+    nqb, nkb = -(-Sq // BLOCK_Q), -(-Skv // BLOCK_KV)
+    if out is None:
+        out = torch.empty((1, 1, nqb, nkb), dtype=torch.uint8,
+                          device=device if device is not None else "cuda")
+    dev = _check_dev(out)
+    if out.dtype != torch.uint8 or out.dim() != 4 or out.shape[2] < nqb or out.shape[3] < nkb \
+            or (out.shape[3] > 1 and out.stride(3) != 1):
+        raise ValueError("out must be uint8 [.., .., >=ceil(Sq/128), >=ceil(Skv/64)], last dim contiguous")
+    flags = (MASK_CAUSAL if causal else 0) | (MASK_WINDOW if window is not None else 0)
+    st = lib.mm_block_mask_create(flags, int(window) if window is not None else 0, Sq, Skv,
+                                  out.data_ptr() if out.numel() else None, out.stride(2), _stream_ptr(dev))
+    if st != 0:
+        raise MaskModsError(st, "mm_block_mask_create")
+    return out
 
 
 def decode_workspace_size(B, Hq, kv_len, D, num_splits=0) -> int:

@@ -35,6 +35,7 @@ SOURCES = [
     "fwd_f16_d64.hip",
     "fwd_f32.hip",
     "decode.hip",
+    "block_mask.hip",
 ]
 
 

@@ -47,7 +47,7 @@ int decode_splits(int32_t B, int32_t Hq, int32_t kv_len, int32_t requested) {
 
 extern "C" {
 
-int32_t mm_version(void) { return 100; }
+int32_t mm_version(void) { return 200; }
 
 size_t mm_fwd_args_size(void) { return sizeof(mm_fwd_args); }
 size_t mm_decode_args_size(void) { return sizeof(mm_decode_args); }
@@ -80,6 +80,7 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
     if (a->mods.mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW | MM_MASK_ROWDROP))
         return MM_ERR_UNSUPPORTED;
     if ((a->mods.mask_flags & MM_MASK_WINDOW) && a->mods.window < 0) return MM_ERR_SHAPE;
+    if (a->mods.block_mask && bad_strides(a->mods.block_mask_strides, 3)) return MM_ERR_STRIDE;
     if (!isfinite(a->scale)) return MM_ERR_SHAPE;
     if (bad_strides(a->q_strides, 3) || bad_strides(a->k_strides, 3) || bad_strides(a->v_strides, 3) ||
         bad_strides(a->o_strides, 3))
@@ -121,10 +122,16 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
     p.rowdrop = (a->mods.mask_flags & MM_MASK_ROWDROP) ? 1 : 0;
     p.rd_seed = a->mods.rowdrop_seed;
     p.rd_thr = a->mods.rowdrop_threshold;
+    p.bm = a->mods.block_mask;
+    p.bm_sb = a->mods.block_mask_strides[0];
+    p.bm_sh = a->mods.block_mask_strides[1];
+    p.bm_sq = a->mods.block_mask_strides[2];
+    static_assert(MM_BLOCK_Q == kBlockQ && MM_BLOCK_KV == kBlockKV, "block-mask granularity");
 
     int mask = 0;
     if (a->causal || (a->mods.mask_flags & MM_MASK_CAUSAL)) mask |= MASK_CAUSAL;
     if (a->mods.mask_flags & MM_MASK_WINDOW) mask |= MASK_WINDOW;
+    if (a->mods.block_mask) mask |= MASK_BLOCK;
     const bool alibi = a->mods.score_mod == MM_SCORE_ALIBI;
     hipStream_t s = (hipStream_t)stream;
 
@@ -139,6 +146,21 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
         else
             e = a->D == 64 ? launch_fwd_mfma_f16_d64(p, alibi, mask, s) : launch_fwd_mfma_f16_d128(p, alibi, mask, s);
     }
+    return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
+}
+
+mm_status mm_block_mask_create(uint32_t mask_flags, int32_t window, int32_t Sq, int32_t Skv, uint8_t *out,
+                               int64_t ld, void *stream) {
+    if (mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW)) return MM_ERR_UNSUPPORTED;
+    if (Sq < 0 || Skv < 0) return MM_ERR_SHAPE;
+    if ((mask_flags & MM_MASK_WINDOW) && window < 0) return MM_ERR_SHAPE;
+    const int64_t nkb = ((int64_t)Skv + MM_BLOCK_KV - 1) / MM_BLOCK_KV;
+    const int64_t nqb = ((int64_t)Sq + MM_BLOCK_Q - 1) / MM_BLOCK_Q;
+    if (nkb == 0 || nqb == 0) return MM_OK;
+    if (!out) return MM_ERR_NULL;
+    if (ld < nkb) return MM_ERR_STRIDE;
+    const hipError_t e = launch_block_mask(out, ld, Sq, Skv, (mask_flags & MM_MASK_CAUSAL) != 0,
+                                           (mask_flags & MM_MASK_WINDOW) ? window : -1, (hipStream_t)stream);
     return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
 }
 

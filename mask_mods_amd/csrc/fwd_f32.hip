@@ -3,7 +3,8 @@
 // The correctness path for fp32 tensors (no performance target): one thread owns one
 // query row, keeps q and the output accumulator in registers and streams every
 // visible key with an online softmax in fp32. Same semantics and mask handling as the
-// MFMA path: scale, then score_mod, then mask_mod; fully masked rows give 0 / -inf.
+// MFMA path: scale, then score_mod, then mask_mod (and the block mask); fully masked
+// rows give 0 / -inf.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,9 +32,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p, int alibi, int
     }
     const float slope2 = alibi ? (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e : 0.f;
 
+    // with a block mask, full blocks bypass the predicates: test each key instead of
+    // narrowing the range
+    const uint8_t *bm_row = p.bm ? p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)(row / kBlockQ) * p.bm_sq : nullptr;
     int j_lo = 0, j_hi = p.Skv;
-    if (mask & MASK_CAUSAL) j_hi = min(j_hi, row + 1);
-    if (mask & MASK_WINDOW) {
+    if ((mask & MASK_CAUSAL) && !bm_row) j_hi = min(j_hi, row + 1);
+    if ((mask & MASK_WINDOW) && !bm_row) {
         j_lo = max(j_lo, row - p.window);
         j_hi = min(j_hi, row + p.window + 1);
     }
@@ -43,6 +47,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p, int alibi, int
 
     float m = -INFINITY, l = 0.f;
     for (int j = j_lo; j < j_hi; ++j) {
+        if (bm_row) {
+            const int blk = bm_row[j / kBlockKV];
+            if (blk == 0) continue;
+            if (blk == 1 && (mask & MASK_CAUSAL) && j > row) continue;
+            if (blk == 1 && (mask & MASK_WINDOW) && abs(row - j) > p.window) continue;
+        }
         const float *kr = kg + (int64_t)j * p.k_ss;
         float t = 0.f;
 #pragma unroll

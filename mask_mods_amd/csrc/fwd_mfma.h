@@ -171,8 +171,9 @@ void fwd_mfma_kernel(FwdParams p) {
     // key range this workgroup can see
     const int row_max = min(q0 + BM, p.Sq) - 1;
     int j_lo = 0, j_hi = p.Skv;
-    if (MASK & MASK_CAUSAL) j_hi = min(j_hi, row_max + 1);
-    if (MASK & MASK_WINDOW) {
+    // with a block mask, full blocks bypass the predicates: no analytic key range
+    if ((MASK & MASK_CAUSAL) && !(MASK & MASK_BLOCK)) j_hi = min(j_hi, row_max + 1);
+    if ((MASK & MASK_WINDOW) && !(MASK & MASK_BLOCK)) {
         j_lo = max(0, q0 - p.window);
         if (!(MASK & MASK_CAUSAL)) j_hi = min(j_hi, row_max + p.window + 1);
     }
@@ -250,21 +251,21 @@ void fwd_mfma_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // one tile: DMA the tile NST-1 ahead into (Kn, Vn) while computing on (Kt, Vt)
-    auto tile = [&](int kt, const unsigned char *Kt, const unsigned char *Vt, unsigned char *Kn,
-                    unsigned char *Vn) {
-        // always copy (past the end: the last tile again, into a buffer nobody reads),
-        // so every tile issues the same DMA and the pipeline waits are uniform
-        if (NST > 2) load_tile(min(kt + NST - 1, kt_hi - 1), Kn, Vn);
-        else if (kt + 1 < kt_hi) load_tile(kt + 1, Kn, Vn);
+    // one tile: DMA tile `next` (if >= 0) into (Kn, Vn) while computing tile kt on
+    // (Kt, Vt). `blk` is the tile's block-mask class: 1 = the mask_mod predicates
+    // decide, 2 = every pair kept (predicates not evaluated).
+    auto tile = [&](int kt, int blk, const unsigned char *Kt, const unsigned char *Vt, int next,
+                    unsigned char *Kn, unsigned char *Vn) {
+        if (next >= 0) load_tile(next, Kn, Vn);
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
+        const bool pred = blk == 1;  // predicates apply in this tile
         bool skip = kt >= kt_hi, need_mask = k0 + BN > p.Skv;
-        if (MASK & MASK_CAUSAL) {
+        if ((MASK & MASK_CAUSAL) && pred) {
             skip |= k0 > r_last;
             need_mask |= k0 + BN - 1 > r0;
         }
-        if (MASK & MASK_WINDOW) {
+        if ((MASK & MASK_WINDOW) && pred) {
             skip |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
@@ -306,8 +307,8 @@ void fwd_mfma_kernel(FwdParams p) {
                         if (need_mask) {
                             const int j = k0 + 4 * hi + jo;
                             bool keep = j < p.Skv;
-                            if (MASK & MASK_CAUSAL) keep &= j <= row;
-                            if (MASK & MASK_WINDOW) keep &= abs(row - j) <= p.window;
+                            if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
+                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
                             t = keep ? t : -INFINITY;
                         }
                         sacc[kb][e] = t;
@@ -374,28 +375,79 @@ void fwd_mfma_kernel(FwdParams p) {
         }
     };
 
-    if (kt_lo < kt_hi) {
-#pragma unroll
-        for (int st = 0; st < NST - 1; ++st) load_tile(min(kt_lo + st, kt_hi - 1), KB[st], VB[st]);
-    }
-    kv_barrier<0>();
-    for (int kt = kt_lo; kt < kt_hi; kt += NST) {
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-            if (NST == 2) {
-                if (kt + st < kt_hi) {
-                    tile(kt + st, KB[st], VB[st], KB[(st + 1) % NST], VB[(st + 1) % NST]);
-                    kv_barrier<0>();
+    if (MASK & MASK_BLOCK) {
+        // Walk the non-empty blocks of this q-block's row of the block mask. The row is
+        // read 64 bytes at a time (one per lane) into a register window; a ballot of the
+        // nonzero bytes gives a wave-uniform bitmap, so every wave finds the same
+        // sequence of blocks without LDS, and a new window is loaded once per 64 blocks.
+        const uint8_t *bm_row = p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)qt * p.bm_sq;
+        const int nkb = kt_hi;  // key tiles (64 keys each) of the row
+        int wbase = -64, wv = 0;
+        uint64_t wm = 0;
+        auto next_block = [&](int from, int &val) {
+            while (from < nkb) {
+                if (from >= wbase + 64) {
+                    wbase = from & ~63;
+                    const int t = wbase + lane;
+                    wv = t < nkb ? (int)bm_row[t] : 0;
+                    wm = __builtin_amdgcn_ballot_w64(wv != 0);
                 }
-            } else {
-                // three stages: the copies issued during this tile stay in flight; the
-                // ones issued a tile earlier (the next tile's) must have landed
-                tile(kt + st, KB[st], VB[st], KB[(st + NST - 1) % NST], VB[(st + NST - 1) % NST]);
-                kv_barrier<2 * LOADS>();
+                const uint64_t m = wm & (~0ull << (from - wbase));
+                if (m) {
+                    const int off = (int)__builtin_ctzll(m);
+                    val = __builtin_amdgcn_readlane(wv, off);
+                    return wbase + off;
+                }
+                from = wbase + 64;
+            }
+            val = 0;
+            return nkb;
+        };
+        int cv, nv;
+        int cur = next_block(0, cv);
+        int nxt = cur < nkb ? next_block(cur + 1, nv) : nkb;
+        if (cur < nkb) load_tile(cur, KB[0], VB[0]);
+        kv_barrier<0>();
+        while (cur < nkb) {
+            tile(cur, cv, KB[0], VB[0], nxt < nkb ? nxt : -1, KB[1], VB[1]);
+            kv_barrier<0>();
+            cur = nxt;
+            cv = nv;
+            if (cur >= nkb) break;
+            nxt = next_block(cur + 1, nv);
+            tile(cur, cv, KB[1], VB[1], nxt < nkb ? nxt : -1, KB[0], VB[0]);
+            kv_barrier<0>();
+            cur = nxt;
+            cv = nv;
+            if (cur < nkb) nxt = next_block(cur + 1, nv);
+        }
+    } else {
+        if (kt_lo < kt_hi) {
+#pragma unroll
+            for (int st = 0; st < NST - 1; ++st) load_tile(min(kt_lo + st, kt_hi - 1), KB[st], VB[st]);
+        }
+        kv_barrier<0>();
+        for (int kt = kt_lo; kt < kt_hi; kt += NST) {
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                if (NST == 2) {
+                    if (kt + st < kt_hi) {
+                        tile(kt + st, 1, KB[st], VB[st], kt + st + 1 < kt_hi ? kt + st + 1 : -1,
+                             KB[(st + 1) % NST], VB[(st + 1) % NST]);
+                        kv_barrier<0>();
+                    }
+                } else {
+                    // three stages: always copy (past the end: the last tile again, into a
+                    // buffer nobody reads) so the waits are uniform; the copies issued
+                    // during this tile stay in flight, the next tile's must have landed
+                    tile(kt + st, 1, KB[st], VB[st], min(kt + st + NST - 1, kt_hi - 1),
+                         KB[(st + NST - 1) % NST], VB[(st + NST - 1) % NST]);
+                    kv_barrier<2 * LOADS>();
+                }
             }
         }
+        if (NST > 2) kv_barrier<0>();  // drain the copies issued past the end
     }
-    if (NST > 2) kv_barrier<0>();  // drain the copies issued past the end
 
     // ---- epilogue ----
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -437,8 +489,10 @@ template <typename TT, int D, bool A, int M>
 hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
     // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic; with
     // causal or window masks, 4-wave tiles (128 rows) follow the diagonal / band more
-    // closely and skip more key tiles, which matters more
+    // closely and skip more key tiles, which matters more; a block mask's q-blocks are
+    // 128 rows, one 4-wave workgroup each
     constexpr int NW = M == 0 ? MM_FWD_NW : MM_FWD_NW_MASKED, NST = MM_FWD_NST;
+    static_assert(!(M & MASK_BLOCK) || NW == 4, "block masks use 128-row workgroups");
     p.n_qtiles = (p.Sq + 32 * NW - 1) / (32 * NW);
     const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(64 * NW);
     fwd_mfma_kernel<TT, D, A, M, NW, NST><<<grid, block, 0, s>>>(p);
@@ -447,16 +501,15 @@ hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
 
 template <typename TT, int D>
 hipError_t launch_fwd_mfma(const FwdParams &p, bool alibi, int mask, hipStream_t s) {
-    switch ((alibi ? 4 : 0) + (mask & 3)) {
-        case 0: return launch_fwd_mfma_one<TT, D, false, 0>(p, s);
-        case 1: return launch_fwd_mfma_one<TT, D, false, 1>(p, s);
-        case 2: return launch_fwd_mfma_one<TT, D, false, 2>(p, s);
-        case 3: return launch_fwd_mfma_one<TT, D, false, 3>(p, s);
-        case 4: return launch_fwd_mfma_one<TT, D, true, 0>(p, s);
-        case 5: return launch_fwd_mfma_one<TT, D, true, 1>(p, s);
-        case 6: return launch_fwd_mfma_one<TT, D, true, 2>(p, s);
-        default: return launch_fwd_mfma_one<TT, D, true, 3>(p, s);
+#define MM_CASE(A, M) case (A) * 8 + (M): return launch_fwd_mfma_one<TT, D, (A) != 0, (M)>(p, s);
+    switch ((alibi ? 8 : 0) + (mask & 7)) {
+        MM_CASE(0, 0) MM_CASE(0, 1) MM_CASE(0, 2) MM_CASE(0, 3)
+        MM_CASE(0, 4) MM_CASE(0, 5) MM_CASE(0, 6) MM_CASE(0, 7)
+        MM_CASE(1, 0) MM_CASE(1, 1) MM_CASE(1, 2) MM_CASE(1, 3)
+        MM_CASE(1, 4) MM_CASE(1, 5) MM_CASE(1, 6) MM_CASE(1, 7)
+        default: return hipErrorInvalidValue;
     }
+#undef MM_CASE
 }
 
 }  // namespace mm

@@ -7,7 +7,10 @@
 
 namespace mm {
 
-enum { MASK_CAUSAL = 1, MASK_WINDOW = 2 };
+enum { MASK_CAUSAL = 1, MASK_WINDOW = 2, MASK_BLOCK = 4 };
+
+// block-mask granularity: query rows x keys per block
+constexpr int kBlockQ = 128, kBlockKV = 64;
 
 // Forward attention, one launch. Strides are in elements.
 struct FwdParams {
@@ -25,6 +28,8 @@ struct FwdParams {
     int rowdrop;           // nonzero: rows with fmix32(seed ^ row) < thr are fully masked
     uint32_t rd_seed, rd_thr;
     int n_qtiles;          // query tiles per (b, h)
+    const uint8_t *bm;     // block mask or nullptr: byte b*bm_sb + h*bm_sh + qblk*bm_sq + kblk
+    int64_t bm_sb, bm_sh, bm_sq;
 };
 
 // Decode split pass + merge. Strides are in elements.
@@ -55,5 +60,8 @@ hipError_t launch_fwd_mfma_f16_d64(const FwdParams &p, bool alibi, int mask, hip
 hipError_t launch_fwd_mfma_f16_d128(const FwdParams &p, bool alibi, int mask, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams &p, int D, bool alibi, int mask, hipStream_t s);
 hipError_t launch_decode(const DecParams &p, int dtype, int D, hipStream_t s);
+// window < 0: no window predicate
+hipError_t launch_block_mask(uint8_t *out, int64_t ld, int Sq, int Skv, bool causal, int window,
+                             hipStream_t s);
 
 }  // namespace mm

@@ -133,3 +133,13 @@ def sample_rows(seed: int, B: int, H: int, S: int, n_random: int = 64) -> np.nda
         rows.append(bh * S + S - 1)
     rows.extend(g.integers(0, B * H * S, size=n_random).tolist())
     return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def random_block_mask(seed: int, shape, p_empty: float = 0.4, p_full: float = 0.3) -> np.ndarray:
+    """uint8 block classes drawn i.i.d.: 0 with p_empty, 2 with p_full, else 1.
+
+    A stand-in for a BlockMask built from an arbitrary mask_mod: any mix of empty,
+    full and partial blocks, in any order along a row.
+    """
+    u = rng(seed).random(shape)
+    return np.where(u < p_empty, 0, np.where(u < p_empty + p_full, 2, 1)).astype(np.uint8)

@@ -150,3 +150,28 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
     if rows is None:
         return out.reshape(B, Hq, Sq, D), lse.reshape(B, Hq, Sq)
     return out, lse
+
+
+def block_classes(Sq: int, Skv: int, *, causal: bool = False, window=None) -> np.ndarray:
+    """Block-mask classes of the causal / sliding-window predicates, by brute force.
+
+    Evaluates the predicates (causal: kv_idx <= q_idx; window: |q_idx - kv_idx| <= w)
+    on every pair (q_idx < Sq, kv_idx < Skv) and classifies each block of BLOCK_Q x
+    BLOCK_KV pairs: 0 if no pair is kept, 2 if every pair is kept, else 1 (the classes
+    the oracle's ``block_mask`` argument reads). Returns uint8 [ceil(Sq/128), ceil(Skv/64)].
+    """
+    nqb, nkb = -(-Sq // BLOCK_Q), -(-Skv // BLOCK_KV)
+    out = np.zeros((nqb, nkb), dtype=np.uint8)
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Skv)[None, :]
+    for qb in range(nqb):
+        ii = i[qb * BLOCK_Q:(qb + 1) * BLOCK_Q]
+        for kb in range(nkb):
+            jj = j[:, kb * BLOCK_KV:(kb + 1) * BLOCK_KV]
+            keep = np.ones((ii.shape[0], jj.shape[1]), dtype=bool)
+            if causal:
+                keep &= jj <= ii
+            if window is not None:
+                keep &= np.abs(ii - jj) <= window
+            out[qb, kb] = 2 if keep.all() else (1 if keep.any() else 0)
+    return out

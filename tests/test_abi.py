@@ -34,7 +34,7 @@ def test_struct_layouts_match():
     lib = mm.load_library()
     assert lib.mm_fwd_args_size() == ctypes.sizeof(mm.FwdArgs)
     assert lib.mm_decode_args_size() == ctypes.sizeof(mm.DecodeArgs)
-    assert lib.mm_version() >= 100
+    assert lib.mm_version() >= 200
 
 
 def test_status_strings():
@@ -82,6 +82,7 @@ def _fwd(**kw):
     (dict(k_strides=mm._I64x3(100, 12, 128)), STRIDE),
     (dict(q=FAKE + 2), STRIDE),
     (dict(scale=float("nan")), SHAPE),
+    (dict(mods_block_mask=FAKE, mods_block_mask_strides=mm._I64x3(0, -4, 1)), STRIDE),
     (dict(B=0), OK),
     (dict(Sq=0), OK),
 ])
@@ -142,3 +143,19 @@ def test_decode_workspace_and_splits():
     for B, L in [(1, 1000), (8, 4096), (1, 10 ** 7), (64, 32768)]:
         s = mm.decode_auto_splits(B, 32, L)
         assert 1 <= s <= min(256, -(-L // 256))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 0, 128, 128, FAKE, 2), UNSUP),          # row drop is not a block predicate
+    ((8, 0, 128, 128, FAKE, 2), UNSUP),
+    ((2, -1, 128, 128, FAKE, 2), SHAPE),         # window < 0
+    ((1, 0, -1, 128, FAKE, 2), SHAPE),
+    ((1, 0, 128, 128, None, 2), NULL),
+    ((1, 0, 128, 129, FAKE, 2), STRIDE),         # ld below ceil(129/64) = 3
+    ((1, 0, 0, 128, None, 0), OK),               # nothing to write
+    ((3, 5, 128, 0, None, 0), OK),
+])
+def test_block_mask_create_rejects_before_launch(args, status):
+    lib = mm.load_library()
+    fl, w, sq, skv, out, ld = args
+    assert lib.mm_block_mask_create(fl, w, sq, skv, out, ld, None) == status

@@ -1,0 +1,225 @@
+"""GPU parity of block-sparse attention (mm_attn_fwd with a block mask, and
+mm_block_mask_create) through the C ABI against the oracle.
+
+Every case prints its parameters first so a failing GPU step names itself.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import (F32_ATOL, F32_RTOL, LSE_ATOL, LSE_RTOL, O_ATOL, O_RTOL, assert_parity,
+                     to_f64, to_torch)
+from mask_mods_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+RD = (20240, int(0.05 * 2 ** 32))
+
+
+def _nblocks(Sq, Skv):
+    return -(-Sq // 128), -(-Skv // 64)
+
+
+def _run(B, Hq, Hkv, Sq, Skv, D, dtype, bm, *, causal=False, window=None, alibi=False,
+         rowdrop=False, seed=0, rows=None, bm_view=None):
+    """bm: uint8 numpy [B|1, Hq|1, nqb, nkb]; bm_view: optional function mapping the
+    device copy of bm to the tensor handed to the library (a strided view of it)."""
+    import torch
+    import mask_mods_amd as mm
+    print(f"[block] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {dtype} bm={bm.shape} "
+          f"causal={causal} window={window} alibi={alibi} rowdrop={rowdrop} seed={seed}", flush=True)
+    x = inputs.attention_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
+    q, k, v = (to_torch(x[n], dtype) for n in ("q", "k", "v"))
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    bmd = torch.from_numpy(np.ascontiguousarray(bm)).cuda()
+    if bm_view is not None:
+        bmd = bm_view(bmd)
+    out, lse = mm.attn_fwd(q, k, v, scale, causal=causal, window=window,
+                           score_mod=mm.SCORE_ALIBI if alibi else mm.SCORE_NONE,
+                           rowdrop=RD if rowdrop else None, block_mask=bmd)
+    torch.cuda.synchronize()
+    qd, kd, vd = (inputs.bits_to_f64(x[n], dtype) for n in ("q", "k", "v"))
+    O, L = oracle.attention(qd, kd, vd, scale=scale, causal=causal, window=window, alibi=alibi,
+                            rowdrop=RD if rowdrop else None, rows=rows, block_mask=bm)
+    got_o, got_l = to_f64(out), to_f64(lse)
+    if rows is not None:
+        got_o = got_o.reshape(-1, D)[rows]
+        got_l = got_l.reshape(-1)[rows]
+    if dtype == "f32":
+        assert_parity(got_o, O, F32_ATOL, F32_RTOL, "O")
+        assert_parity(got_l, L, F32_ATOL, F32_RTOL, "LSE")
+    else:
+        assert_parity(got_o, O, O_ATOL, O_RTOL, "O")
+        assert_parity(got_l, L, LSE_ATOL, LSE_RTOL, "LSE")
+    return out, lse
+
+
+PREDS = {
+    "none": dict(),
+    "causal": dict(causal=True),
+    "window": dict(window=100),
+    "causal_window": dict(causal=True, window=256),
+}
+
+
+# ------------------------------------------------------------ random block classes
+@pytest.mark.parametrize("alibi", [False, True])
+@pytest.mark.parametrize("pred", sorted(PREDS))
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_random_classes_matrix(dtype, D, pred, alibi):
+    S = 300  # 3 query blocks (the last 44 rows), 5 key blocks (the last 44 keys)
+    bm = inputs.random_block_mask(1, (1, 2, *_nblocks(S, S)))
+    _run(1, 2, 2, S, S, D, dtype, bm, alibi=alibi, seed=1, **PREDS[pred])
+
+
+@pytest.mark.parametrize("pred", ["none", "causal"])
+def test_long_rows_cross_several_scan_windows(pred):
+    """5000 keys = 79 key blocks: the non-empty blocks are found across two 64-byte scans."""
+    Sq, Skv = 200, 5000
+    bm = inputs.random_block_mask(2, (1, 4, *_nblocks(Sq, Skv)), p_empty=0.8, p_full=0.1)
+    bm[0, 0] = 0
+    bm[0, 0, :, 70] = 2          # only a block beyond the first 64
+    bm[0, 1, :, :] = 0
+    bm[0, 1, :, 63:65] = 1       # straddles the scan boundary
+    _run(1, 4, 2, Sq, Skv, 128, "bf16", bm, seed=2, **PREDS[pred])
+
+
+@pytest.mark.parametrize("bshape", ["11", "B1", "1H", "BH"])
+def test_broadcast_and_gqa(bshape):
+    B, Hq, Hkv, S = 2, 8, 2, 260
+    shape = (B if bshape[0] == "B" else 1, Hq if bshape[1] == "H" else 1, *_nblocks(S, S))
+    bm = inputs.random_block_mask(3, shape)
+    _run(B, Hq, Hkv, S, S, 128, "bf16", bm, causal=True, alibi=True, seed=3)
+
+
+@pytest.mark.parametrize("Sq,Skv,pred", [
+    (200, 700, "none"), (700, 200, "causal"), (129, 1000, "window"), (1, 513, "none"),
+    (1000, 65, "causal_window"),
+])
+def test_cross_attention(Sq, Skv, pred):
+    bm = inputs.random_block_mask(4, (1, 4, *_nblocks(Sq, Skv)), p_empty=0.3, p_full=0.3)
+    _run(1, 4, 2, Sq, Skv, 128, "f16", bm, seed=4, **PREDS[pred])
+
+
+def test_strided_view_of_a_larger_table():
+    """The table may be a strided view: a window into a larger [B, H, nqb+2, nkb+5] one."""
+    import torch
+    B, H, S = 2, 3, 384
+    nqb, nkb = _nblocks(S, S)
+    big = inputs.random_block_mask(6, (B, H, nqb + 2, nkb + 5))
+    view = big[:, :, 1:1 + nqb, 2:2 + nkb]
+    _run(B, H, H, S, S, 128, "bf16", np.ascontiguousarray(view), alibi=True, causal=True, seed=6,
+         bm_view=lambda t: torch.from_numpy(big).cuda()[:, :, 1:1 + nqb, 2:2 + nkb])
+
+
+def test_all_empty_gives_zero_and_neg_inf():
+    S = 256
+    bm = np.zeros((1, 1, *_nblocks(S, S)), dtype=np.uint8)
+    out, lse = _run(1, 2, 2, S, S, 64, "bf16", bm, seed=7)
+    assert np.all(to_f64(out) == 0) and np.all(to_f64(lse) == -np.inf)
+
+
+def test_full_blocks_ignore_predicates():
+    """Every block full: causal and window are not evaluated, the result is dense."""
+    S = 320
+    bm = np.full((1, 1, *_nblocks(S, S)), 2, dtype=np.uint8)
+    _run(1, 2, 2, S, S, 128, "bf16", bm, causal=True, window=10, seed=8)
+
+
+def test_reserved_values_act_as_full():
+    import torch
+    import mask_mods_amd as mm
+    S = 256
+    nb = _nblocks(S, S)
+    bm = inputs.random_block_mask(9, (1, 2, *nb))
+    alt = bm.copy()
+    alt[alt == 2] = np.where(np.arange((alt == 2).sum()) % 2 == 0, 3, 255)
+    x = inputs.attention_inputs(9, 1, 2, 2, S, S, 128, "bf16")
+    q, k, v = (to_torch(x[n], "bf16") for n in ("q", "k", "v"))
+    o1, l1 = mm.attn_fwd(q, k, v, causal=True, block_mask=torch.from_numpy(bm).cuda())
+    o2, l2 = mm.attn_fwd(q, k, v, causal=True, block_mask=torch.from_numpy(alt).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_rowdrop_applies_inside_blocks():
+    S = 512
+    bm = inputs.random_block_mask(10, (1, 4, *_nblocks(S, S)), p_empty=0.2)
+    _run(1, 4, 4, S, S, 128, "bf16", bm, causal=True, rowdrop=True, seed=10)
+
+
+@pytest.mark.parametrize("pred", ["none", "causal_window"])
+def test_f32_path(pred):
+    S = 200
+    bm = inputs.random_block_mask(11, (1, 2, *_nblocks(S, S)))
+    _run(1, 2, 1, S, S, 64, "f32", bm, seed=11, **PREDS[pred])
+
+
+def test_empty_keys_and_single_row():
+    bm = np.full((1, 1, 1, 1), 2, dtype=np.uint8)
+    _run(1, 2, 2, 1, 1, 128, "bf16", bm, seed=12)
+    bm = np.full((1, 1, 1, 0), 2, dtype=np.uint8)
+    out, lse = _run(1, 2, 2, 5, 0, 128, "bf16", bm, seed=12)
+    assert np.all(to_f64(lse) == -np.inf)
+
+
+# ------------------------------------------------------------ classes of the built-in predicates
+@pytest.mark.parametrize("Sq,Skv,causal,window", [
+    (1024, 1024, True, None), (1000, 777, True, None), (2048, 2048, False, 256),
+    (2048, 2048, True, 256), (300, 5000, False, 1000), (129, 65, True, 0), (5, 3, False, None),
+])
+def test_create_matches_brute_force(Sq, Skv, causal, window):
+    import torch
+    import mask_mods_amd as mm
+    print(f"[block create] Sq={Sq} Skv={Skv} causal={causal} window={window}", flush=True)
+    got = mm.block_mask_create(Sq, Skv, causal=causal, window=window)
+    torch.cuda.synchronize()
+    want = oracle.block_classes(Sq, Skv, causal=causal, window=window)
+    np.testing.assert_array_equal(got[0, 0].cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("pred", ["causal", "causal_window", "window"])
+def test_created_mask_equals_predicates_alone(pred):
+    """Block-sparse with the created classes: same result as the predicates alone, to the
+    bit for causal (the same tiles are visited in the same order with the same masking),
+    and to the oracle in every case."""
+    import torch
+    import mask_mods_amd as mm
+    S = 2000
+    kw = PREDS[pred]
+    bm = mm.block_mask_create(S, S, **kw)
+    out, lse = _run(1, 4, 4, S, S, 128, "bf16", bm.cpu().numpy(), seed=13, **kw,
+                    bm_view=lambda t: bm)
+    if pred == "causal":
+        x = inputs.attention_inputs(13, 1, 4, 4, S, S, 128, "bf16")
+        q, k, v = (to_torch(x[n], "bf16") for n in ("q", "k", "v"))
+        o2, l2 = mm.attn_fwd(q, k, v, float(np.float32(1 / math.sqrt(128))), causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+# ------------------------------------------------------------ full size, sampled rows
+@pytest.mark.parametrize("pred", ["none", "causal"])
+def test_config_8192_half_sparse_sampled(pred):
+    B, H, S = 2, 32, 8192
+    bm = inputs.random_block_mask(14, (B, H, *_nblocks(S, S)), p_empty=0.5, p_full=0.25)
+    rows = inputs.sample_rows(14, B, H, S, n_random=64)
+    _run(B, H, H, S, S, 128, "bf16", bm, seed=14, rows=rows, **PREDS[pred])
+
+
+def test_config_8192_causal_block_mask_bitwise():
+    """The created causal classes at full size give the plain causal kernel's bits."""
+    import torch
+    import mask_mods_amd as mm
+    B, H, S = 2, 32, 8192
+    print(f"[block] causal bitwise B={B} H={H} S={S}", flush=True)
+    x = inputs.attention_inputs(15, B, H, H, S, S, 128, "bf16")
+    q, k, v = (to_torch(x[n], "bf16") for n in ("q", "k", "v"))
+    bm = mm.block_mask_create(S, S, causal=True)
+    o1, l1 = mm.attn_fwd(q, k, v, causal=True, block_mask=bm)
+    o2, l2 = mm.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

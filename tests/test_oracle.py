@@ -491,3 +491,47 @@ def test_block_mask_closed_form_counts():
             assert L[0, 0, i] == -np.inf
         else:
             assert L[0, 0, i] == pytest.approx(math.log(n), abs=1e-14)
+
+
+# ------------------------------------------------ block classes of the built-in predicates
+def test_block_classes_causal_closed_form():
+    """Causal, S = n*128: q-block qb keeps key blocks kb < 2qb whole, 2qb and 2qb+1 in part."""
+    n = 5
+    c = oracle.block_classes(128 * n, 128 * n, causal=True)
+    assert c.shape == (n, 2 * n)
+    for qb in range(n):
+        for kb in range(2 * n):
+            want = 2 if kb < 2 * qb else (1 if kb <= 2 * qb + 1 else 0)
+            assert c[qb, kb] == want, (qb, kb)
+    assert (c == 2).sum() == n * (n - 1) and (c == 1).sum() == 2 * n
+
+
+def test_block_classes_no_predicate_all_full_and_ragged_shape():
+    c = oracle.block_classes(300, 130)
+    assert c.shape == (3, 3) and np.all(c == 2)
+    assert oracle.block_classes(0, 64).shape == (0, 1)
+
+
+def test_block_classes_window_band():
+    """Window w = 64, S = 512: a key block is empty iff every pair is more than 64 apart."""
+    w = 64
+    c = oracle.block_classes(512, 512, window=w)
+    for qb in range(4):
+        for kb in range(8):
+            i0, i1, j0, j1 = 128 * qb, 128 * qb + 127, 64 * kb, 64 * kb + 63
+            nearest = max(0, j0 - i1, i0 - j1)
+            farthest = max(abs(i0 - j1), abs(i1 - j0))
+            want = 0 if nearest > w else (2 if farthest <= w else 1)
+            assert c[qb, kb] == want
+
+
+@pytest.mark.parametrize("Sq,Skv,causal,window", [
+    (300, 300, True, None), (257, 400, False, 70), (400, 190, True, 100), (129, 1000, False, None)])
+def test_block_classes_leave_attention_unchanged(Sq, Skv, causal, window):
+    """Attention with the derived classes equals attention with the predicates alone."""
+    q, k, v = _rand(1, 2, 1, Sq, Skv, 16, seed=11)
+    c = oracle.block_classes(Sq, Skv, causal=causal, window=window)[None, None]
+    O0, L0 = oracle.attention(q, k, v, scale=0.3, causal=causal, window=window)
+    O1, L1 = oracle.attention(q, k, v, scale=0.3, causal=causal, window=window, block_mask=c)
+    np.testing.assert_array_equal(L0, L1)
+    np.testing.assert_array_equal(O0, O1)
