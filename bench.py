@@ -308,11 +308,20 @@ def main():
             "sliding_window": dict(window=W, mask_flags=mm.MASK_CAUSAL),
             "causal_via_mask": dict(mask_flags=mm.MASK_CAUSAL),
         }
+        # block-sparse: the causal classes from mm_block_mask_create, and an i.i.d. table
+        # with half of the blocks empty (a quarter full, a quarter partial, no predicate)
+        nqb, nkb = S // mm.BLOCK_Q, S // mm.BLOCK_KV
+        bm_causal = mm.block_mask_create(S, S, causal=True)
+        bm_rand_np = inputs.random_block_mask(7, (B, H, nqb, nkb), p_empty=0.5, p_full=0.25)
+        bm_rand = torch.from_numpy(bm_rand_np).to(dev)
+        specs["block_causal"] = dict(causal=True, block_mask=bm_causal)
+        specs["block_sparse_50"] = dict(block_mask=bm_rand)
+        block_pairs = int((bm_rand_np != 0).sum()) * mm.BLOCK_Q * mm.BLOCK_KV
         for name, kw in specs.items():
-            for _ in range(3):
+            for _ in range(5):
                 mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            n = 10
+            n = 20
             e0.record(stream)
             for _ in range(n):
                 mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw)
@@ -320,8 +329,10 @@ def main():
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / n * 1e-3
             dense = fwd_flops(B, H, S, S, D)
-            if name in ("causal", "causal_via_mask"):
+            if name in ("causal", "causal_via_mask", "block_causal"):
                 alg = dense / 2
+            elif name == "block_sparse_50":
+                alg = 4.0 * D * block_pairs  # block_pairs: kept pairs summed over (b, h)
             elif name == "sliding_window":
                 alg = 4.0 * B * H * D * window_pairs(S, W)
             else:
