@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+MFMA_FP8_PEAK_TFLOPS = 5033.2    # twice the bf16 rate (dense fp8)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 PAGES_NO_MOD_MI300X_TFLOPS = 470.1  # FlyDSL PR #931 report, no_mod at this workload (MI300X)
 
@@ -317,19 +318,29 @@ def main():
         specs["block_causal"] = dict(causal=True, block_mask=bm_causal)
         specs["block_sparse_50"] = dict(block_mask=bm_rand)
         block_pairs = int((bm_rand_np != 0).sum()) * mm.BLOCK_Q * mm.BLOCK_KV
+        # fp8 (e4m3) inputs: the same draws quantised per tensor on the device
+        def to_fp8(t):
+            s = (t.float().abs().max() / 448.0).item()
+            return (t.float() / s).to(torch.float8_e4m3fn), s
+        (q8, sq), (k8, sk), (v8, sv) = to_fp8(q), to_fp8(k), to_fp8(v)
+        fp8_kw = dict(q=q8, k=k8, v=v8, descale=(sq, sk, sv))
+        specs["fp8_no_mod"] = dict(fp8_kw)
+        specs["fp8_causal"] = dict(fp8_kw, causal=True)
         for name, kw in specs.items():
+            kw = dict(kw)
+            qq, kk, vv = kw.pop("q", q), kw.pop("k", k), kw.pop("v", v)
             for _ in range(5):
-                mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw)
+                mm.attn_fwd(qq, kk, vv, scale, out=out, lse=lse, **kw)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             n = 20
             e0.record(stream)
             for _ in range(n):
-                mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw)
+                mm.attn_fwd(qq, kk, vv, scale, out=out, lse=lse, **kw)
             e1.record(stream)
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / n * 1e-3
             dense = fwd_flops(B, H, S, S, D)
-            if name in ("causal", "causal_via_mask", "block_causal"):
+            if name in ("causal", "causal_via_mask", "block_causal", "fp8_causal"):
                 alg = dense / 2
             elif name == "block_sparse_50":
                 alg = 4.0 * D * block_pairs  # block_pairs: kept pairs summed over (b, h)
@@ -341,6 +352,8 @@ def main():
                    "tflops_algorithmic": round(alg / t / 1e12, 1)}
             if name == "causal":
                 ent["tflops_causal_half"] = round(dense / 2 / t / 1e12, 1)
+            if name.startswith("fp8"):
+                ent["frac_fp8_peak"] = round(alg / t / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4)
             ent["latency_vs_no_mod"] = round(t / fwd_avg_s, 3)
             cases[name] = ent
 

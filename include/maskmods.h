@@ -58,7 +58,9 @@ typedef enum {
     MM_ERR_WORKSPACE = -7    /* decode workspace NULL or too small              */
 } mm_status;
 
-typedef enum { MM_F32 = 0, MM_F16 = 1, MM_BF16 = 2 } mm_dtype;
+/* MM_FP8_E4M3: OCP 8-bit float (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * max 448; what torch calls float8_e4m3fn), forward only; the output is bf16. */
+typedef enum { MM_F32 = 0, MM_F16 = 1, MM_BF16 = 2, MM_FP8_E4M3 = 3 } mm_dtype;
 
 /* score_mod(score, b, h, q_idx, kv_idx) -> score, applied to the scaled score */
 typedef enum {
@@ -109,7 +111,8 @@ typedef struct mm_fwd_args {
     const void *v;        /* [B, Hkv, Skv, D] dtype                                   */
     void *out;            /* [B, Hq, Sq, D]  dtype                                    */
     float *lse;           /* [B, Hq, Sq] fp32 contiguous, or NULL                     */
-    int32_t dtype;        /* mm_dtype: MM_BF16, MM_F16 (MFMA path) or MM_F32           */
+    int32_t dtype;        /* mm_dtype: MM_BF16, MM_F16, MM_FP8_E4M3 (MFMA paths) or
+                             MM_F32; `out` has this dtype, except bf16 for fp8 inputs   */
     int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128}                                 */
     int64_t q_strides[3]; /* elements, for b, h, s                                    */
     int64_t k_strides[3];
@@ -118,6 +121,13 @@ typedef struct mm_fwd_args {
     float scale;          /* multiplies Q K^T before any mod                          */
     int32_t causal;       /* nonzero: same predicate as MM_MASK_CAUSAL                */
     mm_mods mods;
+    /* MM_FP8_E4M3 only (ignored otherwise): per-tensor dequantisation factors, finite
+     * and > 0. The attention is that of the real tensors descale_x * X8: the score is
+     * scale * descale_q * descale_k * (Q8 . K8) and O is descale_v * softmax(...) V8.
+     * The probabilities are rounded to e4m3 (round to nearest even) before the second
+     * product and the row sum is taken over those rounded values; 16-byte aligned
+     * bases and strides that are multiples of 16 elements are required. */
+    float descale_q, descale_k, descale_v;
 } mm_fwd_args;
 
 typedef struct mm_decode_args {

@@ -27,7 +27,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # MASKMODS_LIB may point at another build of the library (e.g. a tuning variant)
 _LIB_PATH = os.environ.get("MASKMODS_LIB") or os.path.join(_PKG, "libmaskmods.so")
 
-MM_F32, MM_F16, MM_BF16 = 0, 1, 2
+MM_F32, MM_F16, MM_BF16, MM_FP8_E4M3 = 0, 1, 2, 3
 SCORE_NONE, SCORE_ALIBI = 0, 1
 MASK_CAUSAL, MASK_WINDOW, MASK_ROWDROP = 1, 2, 4
 ROWDROP_5PCT = int(0.05 * 2 ** 32)  # threshold that drops ~5% of rows
@@ -75,6 +75,7 @@ class FwdArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
         ("mods", _Mods),
+        ("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float), ("descale_v", ctypes.c_float),
     ]
 
 
@@ -142,7 +143,8 @@ def _torch():
 
 def _dtype_code(t) -> int:
     torch = _torch()
-    m = {torch.float32: MM_F32, torch.float16: MM_F16, torch.bfloat16: MM_BF16}
+    m = {torch.float32: MM_F32, torch.float16: MM_F16, torch.bfloat16: MM_BF16,
+         torch.float8_e4m3fn: MM_FP8_E4M3}
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -170,11 +172,13 @@ def _check_dev(*ts):
 
 
 def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_slopes=None,
-             mask_flags=0, window=None, rowdrop=None, block_mask=None, return_lse=True,
-             out=None, lse=None):
+             mask_flags=0, window=None, rowdrop=None, block_mask=None, descale=None,
+             return_lse=True, out=None, lse=None):
     """Fused attention forward.
 
-    q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (bf16, f16 or f32; D in {64,128}).
+    q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (bf16, f16, f32 or float8_e4m3fn; D in {64,128}).
+    fp8 inputs: ``descale=(dq, dk, dv)`` gives the per-tensor factors of the real
+    tensors (dq * q etc., default 1); the output is bf16.
     score_mod: SCORE_NONE or SCORE_ALIBI (or the string "alibi").
     mask_flags: OR of MASK_CAUSAL / MASK_WINDOW / MASK_ROWDROP; ``window`` sets
     MASK_WINDOW, ``rowdrop=(seed, threshold)`` sets MASK_ROWDROP.
@@ -193,8 +197,9 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
         raise ValueError("q/k/v shapes or dtypes disagree")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    fp8 = q.dtype == torch.float8_e4m3fn
     if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=dev)
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16 if fp8 else q.dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
@@ -242,6 +247,7 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
     a.mods.rowdrop_seed = seed & 0xFFFFFFFF
     a.mods.rowdrop_threshold = thr & 0xFFFFFFFF
     a.mods.alibi_slopes = alibi_slopes.data_ptr() if alibi_slopes is not None else None
+    a.descale_q, a.descale_k, a.descale_v = (1.0, 1.0, 1.0) if descale is None else map(float, descale)
     a.mods.block_mask = block_mask.data_ptr() if block_mask is not None and block_mask.numel() else None
     a.mods.block_mask_strides = _I64x3(*bm_strides)
     st = lib.mm_attn_fwd(ctypes.byref(a), _stream_ptr(dev))

@@ -33,6 +33,8 @@ SOURCES = [
     "fwd_bf16_d64.hip",
     "fwd_f16_d128.hip",
     "fwd_f16_d64.hip",
+    "fwd_fp8_d128.hip",
+    "fwd_fp8_d64.hip",
     "fwd_f32.hip",
     "decode.hip",
     "block_mask.hip",

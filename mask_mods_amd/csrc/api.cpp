@@ -25,9 +25,9 @@ bool bad_strides(const int64_t *s, int n) {
 // 16-byte vector loads/stores on the 16-bit paths: pointers 16-byte aligned and every
 // stride a multiple of 8 elements.
 bool misaligned16(const void *p) { return ((uintptr_t)p & 15u) != 0; }
-bool strides_not_mult8(const int64_t *s, int n) {
+bool strides_not_mult(const int64_t *s, int n, int m) {
     for (int i = 0; i < n; ++i)
-        if (s[i] % 8 != 0) return true;
+        if (s[i] % m != 0) return true;
     return false;
 }
 
@@ -72,7 +72,12 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
     const bool no_rows = (int64_t)a->B * a->Hq * a->Sq == 0;
     if ((!a->q || !a->out) && !no_rows) return MM_ERR_NULL;
     if ((!a->k || !a->v) && (int64_t)a->B * a->Hkv * a->Skv != 0) return MM_ERR_NULL;
-    if (a->dtype != MM_F32 && a->dtype != MM_F16 && a->dtype != MM_BF16) return MM_ERR_DTYPE;
+    if (a->dtype != MM_F32 && a->dtype != MM_F16 && a->dtype != MM_BF16 && a->dtype != MM_FP8_E4M3)
+        return MM_ERR_DTYPE;
+    const bool fp8 = a->dtype == MM_FP8_E4M3;
+    if (fp8 && !(isfinite(a->descale_q) && isfinite(a->descale_k) && isfinite(a->descale_v) &&
+                 a->descale_q > 0.f && a->descale_k > 0.f && a->descale_v > 0.f))
+        return MM_ERR_SHAPE;
     if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0) return MM_ERR_SHAPE;
     if (a->Hq % a->Hkv != 0) return MM_ERR_SHAPE;
     if (a->D != 64 && a->D != 128) return MM_ERR_UNSUPPORTED;
@@ -88,12 +93,15 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
     if (a->dtype != MM_F32) {
         if (misaligned16(a->q) || misaligned16(a->k) || misaligned16(a->v) || misaligned16(a->out))
             return MM_ERR_STRIDE;
-        if (strides_not_mult8(a->q_strides, 3) || strides_not_mult8(a->k_strides, 3) ||
-            strides_not_mult8(a->v_strides, 3) || strides_not_mult8(a->o_strides, 3))
+        // 16-byte vectors: 8 elements of 16 bits, 16 of fp8 (the bf16 output keeps 8)
+        const int in_mult = fp8 ? 16 : 8;
+        if (strides_not_mult(a->q_strides, 3, in_mult) || strides_not_mult(a->k_strides, 3, in_mult) ||
+            strides_not_mult(a->v_strides, 3, in_mult) || strides_not_mult(a->o_strides, 3, 8))
             return MM_ERR_STRIDE;
-        // the MFMA kernel addresses a 64-key tile with 32-bit byte offsets
-        if ((64 * a->k_strides[2] + a->D) * 2 >= ((int64_t)1 << 31) ||
-            (64 * a->v_strides[2] + a->D) * 2 >= ((int64_t)1 << 31))
+        // the MFMA kernels address a 64-key tile with 32-bit byte offsets
+        const int64_t esz = fp8 ? 1 : 2;
+        if ((64 * a->k_strides[2] + a->D) * esz >= ((int64_t)1 << 31) ||
+            (64 * a->v_strides[2] + a->D) * esz >= ((int64_t)1 << 31))
             return MM_ERR_STRIDE;
     } else {
         if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->out) & 3u) return MM_ERR_STRIDE;
@@ -117,6 +125,11 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
     p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_ss = a->v_strides[2];
     p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_ss = a->o_strides[2];
     p.scale_log2 = a->scale * 1.4426950408889634f;
+    p.v_descale = 1.f;
+    if (fp8) {
+        p.scale_log2 = (float)((double)a->scale * a->descale_q * a->descale_k * 1.4426950408889634);
+        p.v_descale = a->descale_v;
+    }
     p.slopes = a->mods.alibi_slopes;
     p.window = a->mods.window;
     p.rowdrop = (a->mods.mask_flags & MM_MASK_ROWDROP) ? 1 : 0;
@@ -141,7 +154,9 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
         e = launch_fwd_f32(p, a->D, alibi, mask, s);
     } else {
         if ((int64_t)((a->Sq + kFwdBM - 1) / kFwdBM) * a->Hq * a->B > 0x7fffffff) return MM_ERR_SHAPE;
-        if (a->dtype == MM_BF16)
+        if (fp8)
+            e = a->D == 64 ? launch_fwd_fp8_d64(p, alibi, mask, s) : launch_fwd_fp8_d128(p, alibi, mask, s);
+        else if (a->dtype == MM_BF16)
             e = a->D == 64 ? launch_fwd_mfma_bf16_d64(p, alibi, mask, s) : launch_fwd_mfma_bf16_d128(p, alibi, mask, s);
         else
             e = a->D == 64 ? launch_fwd_mfma_f16_d64(p, alibi, mask, s) : launch_fwd_mfma_f16_d128(p, alibi, mask, s);
@@ -191,7 +206,7 @@ mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
         return MM_ERR_STRIDE;
     if (misaligned16(a->q) || misaligned16(a->k_cache) || misaligned16(a->v_cache))
         return MM_ERR_STRIDE;
-    if (strides_not_mult8(a->q_strides, 2) || strides_not_mult8(a->kv_strides, 3)) return MM_ERR_STRIDE;
+    if (strides_not_mult(a->q_strides, 2, 8) || strides_not_mult(a->kv_strides, 3, 8)) return MM_ERR_STRIDE;
     if (((uintptr_t)a->out & 1u) || ((uintptr_t)a->mask & 1u)) return MM_ERR_STRIDE;
     if (a->B == 0) return MM_OK;
 

@@ -1,0 +1,376 @@
+// fwd_fp8.h -- flash-attention forward for gfx950 on fp8 (OCP e4m3) inputs, bf16 output.
+//
+// Same flex semantics and tiling as the 16-bit kernel (fwd_mfma.h): a wave owns 32 query
+// rows, keys stream through LDS in 64-key tiles copied by DMA, both products run in
+// transposed form on the MFMA with fp32 accumulation. Here the MFMA is the gfx950
+// 32x32x64 f8f6f4 instruction with e4m3 operands on both sides:
+//   S^T[j][i] = sum_d K8[j][d] Q8[i][d]    A = K tile (2 x ds_read_b128 per 64 dims),
+//                                          B = Q8^T held in VGPRs
+//   O^T[d][i] += sum_j V8^T[d][j] P8^T[j][i]
+// with the per-tensor dequantisation factors applied outside the products: the Q and
+// K factors multiply the score scale, the V factor the output.
+//
+// P is rounded to e4m3 (round to nearest even) to feed the second product. The lane's
+// 32 scores of a tile (S^T accumulator elements of two 32-key blocks) are exactly the
+// 32 contraction slots it holds in the B operand, taken in accumulator order, so P never
+// moves between lanes. V^T comes from the row-major V tile through ds_read_b64_tr_b8:
+// in each 16-lane group, output lane t receives byte t%8 of the 8 bytes addressed by
+// input lanes 2k + t/8 (k = 0..7); pairs of input lanes read the same key at dims
+// 8 apart, so lane t gets one dim over 8 keys, and four reads give the 32 keys of the
+// lane's slots. The row sum l is taken by one more MFMA with an all-ones A operand
+// on the same rounded P, so O = sum(P8 V) / sum(P8) is normalised consistently.
+//
+// LDS: K and V tiles as 64 rows of D bytes; 16-byte chunks XOR-swizzled by row so the
+// K reads (16 consecutive rows, one chunk) and the transposed V reads (8 keys x 2 chunks
+// per 16 lanes) are free of bank conflicts.
+#pragma once
+
+#include "fwd_common.h"
+
+namespace mm {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    // formats 0/0 = e4m3 for A and B; no block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// two e4m3 values (round to nearest even) into the low or high half of a word
+__device__ __forceinline__ int pack_fp8_lo(float a, float b) { return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false); }
+__device__ __forceinline__ int pack_fp8_hi(float a, float b, int w) { return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, true); }
+
+// Swizzled row-major tile of D one-byte elements per key.
+template <int D>
+struct Tile8 {
+    static constexpr int ROWB = D;       // bytes per key row
+    static constexpr int CH = D / 16;    // 16-byte chunks per row
+    __host__ __device__ static constexpr int swz(int r) {
+        // D = 128: j = (r >> 1) & 7 with its two low bits swapped; D = 64: (r >> 2) & 3
+        return D == 128 ? (((r >> 1) & 1) << 1 | ((r >> 2) & 1) | ((r >> 1) & 4)) : ((r >> 2) & 3);
+    }
+    __host__ __device__ static constexpr int off(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
+};
+
+template <int D, bool ALIBI, int MASK, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_fp8_kernel(FwdParams p) {
+    constexpr int BM = 32 * NW, BN = 64;
+    constexpr int NC = D / 64;   // 64-dim k-steps of Q K^T
+    constexpr int DB = D / 32;   // 32-dim blocks of O^T
+    constexpr int NKB = BN / 32; // 32-key blocks of S^T per tile
+    typedef Tile8<D> TL;
+    constexpr int TILEB = BN * TL::ROWB;   // bytes of one K (or V) tile
+    constexpr int KBLK = TILEB / 1024;     // 1 KB copy blocks per K tile
+    constexpr int NL = 2 * KBLK / NW;      // copy instructions per wave per tile
+    constexpr int RPI = 1024 / TL::ROWB;   // rows per copy block
+    constexpr float kRescale = 8.f;
+    static_assert(NL >= 1 && NL * NW == 2 * KBLK && KBLK % NL == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
+    unsigned char *const KB[2] = {kv0, kv1};
+    unsigned char *const VB[2] = {kv0 + TILEB, kv1 + TILEB};
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt_idx = L % p.n_qtiles;
+    L /= p.n_qtiles;
+    const int h = L % p.Hq;
+    const int b = L / p.Hq;
+    const int qt = (MASK & MASK_CAUSAL) ? (p.n_qtiles - 1 - qt_idx) : qt_idx;
+    const int q0 = qt * BM;
+    const int hk = h / p.group;
+
+    const uint8_t *qg = (const uint8_t *)p.q + b * p.q_sb + h * p.q_sh;
+    const uint8_t *kg = (const uint8_t *)p.k + b * p.k_sb + hk * p.k_sh;
+    const uint8_t *vg = (const uint8_t *)p.v + b * p.v_sb + hk * p.v_sh;
+
+    const int r0 = q0 + wave * 32;
+    const int row = r0 + l32;
+
+    // Q^T fragments (B operand): row `row`, dims 64*c + 32*hi .. +31
+    i32x8 qf[NC];
+    {
+        const bool ok = row < p.Sq;
+        const uint8_t *qr = qg + (int64_t)(ok ? row : 0) * p.q_ss + 32 * hi;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4 x0 = ok ? *(const u32x4 *)(qr + 64 * c) : u32x4{0, 0, 0, 0};
+            const u32x4 x1 = ok ? *(const u32x4 *)(qr + 64 * c + 16) : u32x4{0, 0, 0, 0};
+            qf[c] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        }
+    }
+
+    const int row_max = min(q0 + BM, p.Sq) - 1;
+    int j_lo = 0, j_hi = p.Skv;
+    if ((MASK & MASK_CAUSAL) && !(MASK & MASK_BLOCK)) j_hi = min(j_hi, row_max + 1);
+    if ((MASK & MASK_WINDOW) && !(MASK & MASK_BLOCK)) {
+        j_lo = max(0, q0 - p.window);
+        if (!(MASK & MASK_CAUSAL)) j_hi = min(j_hi, row_max + p.window + 1);
+    }
+    const int kt_lo = j_lo / BN;
+    const int kt_hi = j_hi > j_lo ? (j_hi + BN - 1) / BN : kt_lo;
+
+    float slope2 = 0.f;
+    if (ALIBI) slope2 = (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e;
+    const float c2 = p.scale_log2;
+
+    // K reads: row l32 (+32 per key block), chunks 4c + 2hi + {0, 1}
+    int koff[NC][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        koff[c][0] = TL::off(l32, 4 * c + 2 * hi);
+        koff[c][1] = TL::off(l32, 4 * c + 2 * hi + 1);
+    }
+    // transposed V reads: group G = lane/16, u = lane%16 addresses key
+    // 8*(u/8) + 4*(G/2) + (u/2)%4 (+16 per read), dims 32*db + 16*(G%2) + 8*(u%2)
+    int voff[DB];
+    {
+        const int G = lane >> 4, u = lane & 15;
+        const int key = 8 * (u >> 3) + 4 * (G >> 1) + ((u >> 1) & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) voff[db] = TL::off(key, 2 * db + (G & 1)) + 8 * (u & 1);
+    }
+
+    // copies: wave w moves blocks w*NL .. +NL-1 of the tile pair (K blocks first, then V)
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const bool cp_v = wave_s * NL >= KBLK;
+    const int blk0 = wave_s * NL - (cp_v ? KBLK : 0);
+    const uint8_t *cp_src = cp_v ? vg : kg;
+    const int64_t cp_ss = cp_v ? p.v_ss : p.k_ss;
+    uint32_t goff[NL];
+    int trow[NL], tchunk[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int r = (blk0 + i) * RPI + lane / TL::CH;
+        const int c = (lane % TL::CH) ^ TL::swz(r);
+        trow[i] = r;
+        tchunk[i] = c;
+        goff[i] = (uint32_t)(r * (int)cp_ss + 16 * c);
+    }
+    auto load_tile = [&](int kt, unsigned char *kdst) {
+        const int k0 = kt * BN;
+        const uint32_t dst = lds_addr(kdst) + (cp_v ? (uint32_t)TILEB : 0u) + (uint32_t)blk0 * 1024u;
+        if (k0 + BN <= p.Skv) {
+            const uint8_t *base = cp_src + (int64_t)k0 * cp_ss;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) dma16_sbase(base, goff[i], dst + i * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int gr = min(k0 + trow[i], p.Skv - 1);
+                dma16_vaddr(cp_src + (int64_t)gr * cp_ss + 16 * tchunk[i], dst + i * 1024);
+            }
+        }
+    };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    f32x16 lacc = f32x16{};
+    float m_run = -INFINITY;
+    const int one4 = 0x38383838;  // four e4m3 ones
+    const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
+
+    auto tile = [&](int kt, int blk, const unsigned char *Kt, const unsigned char *Vt, int next,
+                    unsigned char *Kn) {
+        if (next >= 0) load_tile(next, Kn);
+        const int k0 = kt * BN;
+        const int r_last = r0 + 31;
+        const bool pred = blk == 1;
+        bool skip = kt >= kt_hi, need_mask = k0 + BN > p.Skv;
+        if ((MASK & MASK_CAUSAL) && pred) {
+            skip |= k0 > r_last;
+            need_mask |= k0 + BN - 1 > r0;
+        }
+        if ((MASK & MASK_WINDOW) && pred) {
+            skip |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
+            need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
+        }
+        if (skip) return;
+
+        f32x16 sacc[NKB];
+        {
+            u32x4 ka[NKB][NC][2];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        ka[kb][c][e] = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[c][e]);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                sacc[kb] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const u32x4 x0 = ka[kb][c][0], x1 = ka[kb][c][1];
+                    const i32x8 a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                    sacc[kb] = mfma_fp8(a, qf[c], sacc[kb]);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, NKB * NC * 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NKB * NC, 0);
+        }
+        float mloc = -INFINITY, cc;
+        const bool general = ALIBI || need_mask || !(c2 > 0.f);
+        if (general) {
+            const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
+                    float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
+                    if (need_mask) {
+                        const int j = k0 + 4 * hi + jo;
+                        bool keep = j < p.Skv;
+                        if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
+                        if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                        t = keep ? t : -INFINITY;
+                    }
+                    sacc[kb][e] = t;
+                    mloc = fmaxf(mloc, t);
+                }
+            }
+            cc = 1.f;
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
+            mloc *= c2;
+            cc = c2;
+        }
+        mloc = row_max2(mloc);
+        if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescale)) {
+            const float m_new = fmaxf(m_run, mloc);
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            lacc *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float nm = m_run == -INFINITY ? 0.f : -m_run;
+        // P = 2^(t - m) rounded to e4m3; byte i of the operand is accumulator element
+        // i % 16 of key block i / 16
+        int pp[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int kb = w >> 2, e0 = 4 * (w & 3);
+            const float x0 = fast_exp2(fmaf(sacc[kb][e0 + 0], cc, nm));
+            const float x1 = fast_exp2(fmaf(sacc[kb][e0 + 1], cc, nm));
+            const float x2 = fast_exp2(fmaf(sacc[kb][e0 + 2], cc, nm));
+            const float x3 = fast_exp2(fmaf(sacc[kb][e0 + 3], cc, nm));
+            pp[w] = pack_fp8_hi(x2, x3, pack_fp8_lo(x0, x1));
+        }
+        const i32x8 pf = {pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
+        {
+            i32x2 va[DB][4];
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    va[db][r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (MM_LDS i32x2 *)(Vt + voff[db] + 16 * r * TL::ROWB));
+            lacc = mfma_fp8(ones, pf, lacc);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const i32x8 a = {va[db][0][0], va[db][0][1], va[db][1][0], va[db][1][1],
+                                 va[db][2][0], va[db][2][1], va[db][3][0], va[db][3][1]};
+                oacc[db] = mfma_fp8(a, pf, oacc[db]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, DB + 1, 1);
+        }
+    };
+
+    if (MASK & MASK_BLOCK) {
+        BlockWalk walk(p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)qt * p.bm_sq, kt_hi);
+        const int nkb = kt_hi;
+        int cv, nv;
+        int cur = walk.next(0, lane, cv);
+        int nxt = cur < nkb ? walk.next(cur + 1, lane, nv) : nkb;
+        if (cur < nkb) load_tile(cur, KB[0]);
+        kv_barrier<0>();
+        while (cur < nkb) {
+            tile(cur, cv, KB[0], VB[0], nxt < nkb ? nxt : -1, KB[1]);
+            kv_barrier<0>();
+            cur = nxt;
+            cv = nv;
+            if (cur >= nkb) break;
+            nxt = walk.next(cur + 1, lane, nv);
+            tile(cur, cv, KB[1], VB[1], nxt < nkb ? nxt : -1, KB[0]);
+            kv_barrier<0>();
+            cur = nxt;
+            cv = nv;
+            if (cur < nkb) nxt = walk.next(cur + 1, lane, nv);
+        }
+    } else {
+        if (kt_lo < kt_hi) load_tile(kt_lo, KB[0]);
+        kv_barrier<0>();
+        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+            tile(kt, 1, KB[0], VB[0], kt + 1 < kt_hi ? kt + 1 : -1, KB[1]);
+            kv_barrier<0>();
+            if (kt + 1 < kt_hi) {
+                tile(kt + 1, 1, KB[1], VB[1], kt + 2 < kt_hi ? kt + 2 : -1, KB[0]);
+                kv_barrier<0>();
+            }
+        }
+    }
+
+    // ---- epilogue: both lane halves hold the whole row sum in lacc ----
+    const float l_tot = lacc[0];
+    bool dropped = false;
+    if (p.rowdrop) {
+        const uint32_t rid = (uint32_t)(((int64_t)b * p.Hq + h) * p.Sq + row);
+        dropped = fmix32(p.rd_seed ^ rid) < p.rd_thr;
+    }
+    const bool live = l_tot > 0.f && !dropped;
+    const float inv = live ? p.v_descale / l_tot : 0.f;
+    if (row < p.Sq) {
+        uint16_t *og = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
+                                 oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+                *(bf16x4 *)(og + 32 * db + 8 * g4 + 4 * hi) = cvt4(x, BF16{});
+            }
+        }
+        if (hi == 0 && p.lse) {
+            p.lse[((int64_t)b * p.Hq + h) * p.Sq + row] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+    }
+}
+
+template <int D, bool A, int M>
+hipError_t launch_fwd_fp8_one(FwdParams p, hipStream_t s) {
+    constexpr int NW = M == 0 ? 8 : 4;
+    p.n_qtiles = (p.Sq + 32 * NW - 1) / (32 * NW);
+    const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(64 * NW);
+    fwd_fp8_kernel<D, A, M, NW><<<grid, block, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fwd_fp8(const FwdParams &p, bool alibi, int mask, hipStream_t s) {
+#define MM_CASE(A, M) case (A) * 8 + (M): return launch_fwd_fp8_one<D, (A) != 0, (M)>(p, s);
+    switch ((alibi ? 8 : 0) + (mask & 7)) {
+        MM_CASE(0, 0) MM_CASE(0, 1) MM_CASE(0, 2) MM_CASE(0, 3)
+        MM_CASE(0, 4) MM_CASE(0, 5) MM_CASE(0, 6) MM_CASE(0, 7)
+        MM_CASE(1, 0) MM_CASE(1, 1) MM_CASE(1, 2) MM_CASE(1, 3)
+        MM_CASE(1, 4) MM_CASE(1, 5) MM_CASE(1, 6) MM_CASE(1, 7)
+        default: return hipErrorInvalidValue;
+    }
+#undef MM_CASE
+}
+
+}  // namespace mm

@@ -31,16 +31,13 @@
 // is clamped to 0 while it is -inf, and the epilogue guards 1/l).
 #pragma once
 
-#include "common.h"
-#include "kernels.h"
+#include "fwd_common.h"
 
 namespace mm {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-#define MM_LDS __attribute__((address_space(3)))
 
 // row sum helper: acc + p.x + p.y on the 16-bit pair that feeds the PV MFMA
 __device__ __forceinline__ float dot2_ones(uint32_t pair, float acc, BF16) {
@@ -58,13 +55,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, F16) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
-// max of x over lanes l and l ^ 32 (the two halves holding one query row)
-__device__ __forceinline__ float row_max2(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
-}
-
 // Swizzled row-major tile of 16-bit elements, D per row.
 template <int D>
 struct Tile {
@@ -75,40 +65,6 @@ struct Tile {
     }
     __host__ __device__ static constexpr int off(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
 };
-
-// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4). The LDS destination
-// is M0 + 16*lane. Written in asm so the compiler does not track the copy: it would
-// otherwise wait for every copy in flight before reading any LDS buffer it cannot
-// prove disjoint. The kernel orders copies and reads itself (kv_barrier). No output
-// registers; the kernels leave nothing of their own in M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is written on purpose (see above)
-__device__ __forceinline__ void dma16_sbase(const void *gbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 ::"v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_vaddr(const void *gaddr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 ::"v"(gaddr), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const MM_LDS void *)p;
-}
-
-// barrier for the K/V pipeline: waits until this wave has at most VMCNT copies in
-// flight (older copies have landed: the vector-memory counter retires in order) and
-// its LDS reads are done, then synchronises the workgroup.
-template <int VMCNT>
-__device__ __forceinline__ void kv_barrier() {
-    static_assert(VMCNT >= 0 && VMCNT < 64, "vmcnt");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((VMCNT & 15) | ((VMCNT >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-}
 
 template <typename TT, int D, bool ALIBI, int MASK, int NW, int NST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -376,33 +332,9 @@ void fwd_mfma_kernel(FwdParams p) {
     };
 
     if (MASK & MASK_BLOCK) {
-        // Walk the non-empty blocks of this q-block's row of the block mask. The row is
-        // read 64 bytes at a time (one per lane) into a register window; a ballot of the
-        // nonzero bytes gives a wave-uniform bitmap, so every wave finds the same
-        // sequence of blocks without LDS, and a new window is loaded once per 64 blocks.
-        const uint8_t *bm_row = p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)qt * p.bm_sq;
+        BlockWalk walk(p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)qt * p.bm_sq, kt_hi);
         const int nkb = kt_hi;  // key tiles (64 keys each) of the row
-        int wbase = -64, wv = 0;
-        uint64_t wm = 0;
-        auto next_block = [&](int from, int &val) {
-            while (from < nkb) {
-                if (from >= wbase + 64) {
-                    wbase = from & ~63;
-                    const int t = wbase + lane;
-                    wv = t < nkb ? (int)bm_row[t] : 0;
-                    wm = __builtin_amdgcn_ballot_w64(wv != 0);
-                }
-                const uint64_t m = wm & (~0ull << (from - wbase));
-                if (m) {
-                    const int off = (int)__builtin_ctzll(m);
-                    val = __builtin_amdgcn_readlane(wv, off);
-                    return wbase + off;
-                }
-                from = wbase + 64;
-            }
-            val = 0;
-            return nkb;
-        };
+        auto next_block = [&](int from, int &val) { return walk.next(from, lane, val); };
         int cv, nv;
         int cur = next_block(0, cv);
         int nxt = cur < nkb ? next_block(cur + 1, nv) : nkb;

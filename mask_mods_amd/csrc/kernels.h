@@ -30,6 +30,7 @@ struct FwdParams {
     int n_qtiles;          // query tiles per (b, h)
     const uint8_t *bm;     // block mask or nullptr: byte b*bm_sb + h*bm_sh + qblk*bm_sq + kblk
     int64_t bm_sb, bm_sh, bm_sq;
+    float v_descale;       // fp8 inputs: V dequantisation factor (the Q/K ones are in scale_log2)
 };
 
 // Decode split pass + merge. Strides are in elements.
@@ -58,6 +59,8 @@ hipError_t launch_fwd_mfma_bf16_d64(const FwdParams &p, bool alibi, int mask, hi
 hipError_t launch_fwd_mfma_bf16_d128(const FwdParams &p, bool alibi, int mask, hipStream_t s);
 hipError_t launch_fwd_mfma_f16_d64(const FwdParams &p, bool alibi, int mask, hipStream_t s);
 hipError_t launch_fwd_mfma_f16_d128(const FwdParams &p, bool alibi, int mask, hipStream_t s);
+hipError_t launch_fwd_fp8_d64(const FwdParams &p, bool alibi, int mask, hipStream_t s);
+hipError_t launch_fwd_fp8_d128(const FwdParams &p, bool alibi, int mask, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams &p, int D, bool alibi, int mask, hipStream_t s);
 hipError_t launch_decode(const DecParams &p, int dtype, int D, hipStream_t s);
 // window < 0: no window predicate

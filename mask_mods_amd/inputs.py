@@ -59,6 +59,56 @@ def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+# ---- OCP e4m3 ("float8_e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits,
+# no infinities, NaN = S.1111.111, max 448, smallest subnormal 2^-9.
+def _e4m3_table() -> np.ndarray:
+    t = np.empty(256, dtype=np.float64)
+    for c in range(128):
+        e, m = c >> 3, c & 7
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        t[c], t[c | 0x80] = v, -v
+    t[0x7F] = t[0xFF] = np.nan
+    return t
+
+
+E4M3_VALUES = _e4m3_table()
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to e4m3 (nearest, ties to even); |x| must not exceed 448. Returns uint8."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(~np.isfinite(a)) or np.any(a > E4M3_MAX):
+        raise ValueError("e4m3 encoding needs finite values of magnitude <= 448")
+    ex = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    quantum = 2.0 ** (np.maximum(ex, -6) - 3)   # spacing of e4m3 values around a
+    y = np.rint(a / quantum) * quantum           # np.rint rounds half to even
+    pos = E4M3_VALUES[:0x7F]                     # codes 0..126: increasing magnitudes
+    code = np.searchsorted(pos, y).astype(np.uint8)
+    assert np.all(pos[code] == y)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return E4M3_VALUES[np.ascontiguousarray(bits, dtype=np.uint8)]
+
+
+def attention_inputs_fp8(seed: int, B: int, Hq: int, Hkv: int, Sq: int, Skv: int, D: int) -> dict:
+    """N(0,1) Q, K, V (same draws as attention_inputs) quantised per tensor to e4m3:
+    X8 = e4m3(X / s) with s = max|X| / 448 in float32; the real tensor is s * X8.
+    Returns the uint8 bits and the three factors (float32)."""
+    g = rng(seed)
+    out = {"dtype": "fp8"}
+    for name, shape in (("q", (B, Hq, Sq, D)), ("k", (B, Hkv, Skv, D)), ("v", (B, Hkv, Skv, D))):
+        x = g.standard_normal(size=shape, dtype=np.float32)
+        amax = float(np.max(np.abs(x))) if x.size else 1.0
+        s = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+        out[name] = f32_to_e4m3_bits(np.minimum(np.abs(x / s), E4M3_MAX) * np.sign(x))
+        out["descale_" + name] = float(s)
+    return out
+
+
 def normal_bits(g: np.random.Generator, shape, dtype: str) -> np.ndarray:
     """N(0,1) float32 draws encoded in ``dtype``."""
     return f32_to_bits(g.standard_normal(size=shape, dtype=np.float32), dtype)

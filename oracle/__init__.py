@@ -61,7 +61,7 @@ def load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
         _dp, ctypes.c_int64, _ip,
         _bp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        _lp, ctypes.c_int64, _dp, _dp,
+        _lp, ctypes.c_int64, _dp, _dp, _dp, _dp,
     ]
     lib.oracle_attention.restype = ctypes.c_int
     _lib = lib
@@ -93,7 +93,8 @@ def _ptr(a, typ):
 
 
 def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=False,
-              slopes=None, rowdrop=None, add_mask=None, lens=None, rows=None, block_mask=None):
+              slopes=None, rowdrop=None, add_mask=None, lens=None, rows=None, block_mask=None,
+              sensitivity=False):
     """Run the oracle.
 
     q: float64 [B,Hq,Sq,D]; k, v: float64 [B,Hkv,kv_cap,D] (first ``Skv`` keys used,
@@ -103,6 +104,8 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
     (b*Hq + h)*Sq + i (returns O [n,D], LSE [n]).
     block_mask: None or uint8 [B or 1, Hq or 1, ceil(Sq/128), ceil(Skv/64)] with
     0 = block masked, 1 = predicates decide, 2 = block kept (size-1 dims broadcast).
+    sensitivity: also return wsq (per row, sum of squared weights) and wvar (per
+    element, sum_j w_j^2 (V[j,d] - O[d])^2), shaped like LSE and O.
     """
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -129,6 +132,8 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
         n = B * Hq * Sq
     out = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
+    wsq = np.zeros((n,), dtype=np.float64) if sensitivity else None
+    wvar = np.zeros((n, D), dtype=np.float64) if sensitivity else None
     seed, thr = (0, 0) if rowdrop is None else rowdrop
     bm_s = (0, 0, 0)
     if block_mask is not None:
@@ -144,12 +149,16 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
         seed & 0xFFFFFFFF, thr & 0xFFFFFFFF,
         _ptr(add_mask, _dp), mask_ld, _ptr(lens, _ip),
         _ptr(block_mask, _bp), bm_s[0], bm_s[1], bm_s[2],
-        _ptr(rows, _lp), n if rows is not None else 0, _ptr(out, _dp), _ptr(lse, _dp))
+        _ptr(rows, _lp), n if rows is not None else 0, _ptr(out, _dp), _ptr(lse, _dp),
+        _ptr(wsq, _dp), _ptr(wvar, _dp))
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")
     if rows is None:
-        return out.reshape(B, Hq, Sq, D), lse.reshape(B, Hq, Sq)
-    return out, lse
+        res = (out.reshape(B, Hq, Sq, D), lse.reshape(B, Hq, Sq))
+        if sensitivity:
+            res += (wsq.reshape(B, Hq, Sq), wvar.reshape(B, Hq, Sq, D))
+        return res
+    return (out, lse, wsq, wvar) if sensitivity else (out, lse)
 
 
 def block_classes(Sq: int, Skv: int, *, causal: bool = False, window=None) -> np.ndarray:

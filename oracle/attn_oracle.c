@@ -107,8 +107,10 @@ typedef struct {
 #define ORACLE_BLOCK_Q 128
 #define ORACLE_BLOCK_KV 64
 
-/* One query row. s: scratch of Skv doubles. o: D outputs. */
-static void attend_row(const problem *p, int b, int h, int i, double *s, double *o, double *lse)
+/* One query row. s: scratch of Skv doubles. o: D outputs. wsq, wvar: NULL or the
+ * row's first-order sensitivity to relative perturbations of the weights (below). */
+static void attend_row(const problem *p, int b, int h, int i, double *s, double *o, double *lse,
+                       double *wsq, double *wvar)
 {
     const int group = p->Hq / p->Hkv;
     const int hk = h / group;
@@ -145,6 +147,9 @@ static void attend_row(const problem *p, int b, int h, int i, double *s, double 
         if (x > M) M = x;
     }
     for (int d = 0; d < p->D; ++d) o[d] = 0.0;
+    if (wsq) *wsq = 0.0;
+    if (wvar)
+        for (int d = 0; d < p->D; ++d) wvar[d] = 0.0;
     if (M == -INFINITY) {
         *lse = -INFINITY;
         return;
@@ -158,6 +163,21 @@ static void attend_row(const problem *p, int b, int h, int i, double *s, double 
     }
     for (int d = 0; d < p->D; ++d) o[d] /= Lsum;
     *lse = M + log(Lsum);
+    if (!wsq && !wvar) return;
+    /* w_j = exp(s_j - M) / Lsum; if every weight is perturbed to w_j (1 + e_j) (and the
+     * weights renormalised), O_d moves by sum_j e_j w_j (v_jd - O_d) and LSE by
+     * sum_j e_j w_j, to first order. With independent e_j of variance t^2 their standard
+     * deviations are t * sqrt(wvar_d) and t * sqrt(wsq). */
+    for (int j = 0; j < p->Skv; ++j) {
+        if (s[j] == -INFINITY) continue;
+        const double w = exp(s[j] - M) / Lsum;
+        if (wsq) *wsq += w * w;
+        if (wvar)
+            for (int d = 0; d < p->D; ++d) {
+                const double dv = vb[(int64_t)j * p->D + d] - o[d];
+                wvar[d] += w * w * dv * dv;
+            }
+    }
 }
 
 /*
@@ -170,6 +190,10 @@ static void attend_row(const problem *p, int b, int h, int i, double *s, double 
  *   block_mask: NULL or bytes indexed b*bm_sb + h*bm_sh + (i/128)*bm_sq + j/64
  *   rows:  NULL -> every row in order; else nrows flat row ids (b*Hq + h)*Sq + i
  *   out [nrows, D], lse [nrows]
+ *   wsq [nrows], wvar [nrows, D]: NULL, or per row sum_j w_j^2 and per element
+ *          sum_j w_j^2 (V[j,d] - O[d])^2 over the kept keys (w_j the softmax weights):
+ *          the first-order scale of the LSE and O errors that independent relative
+ *          errors in the weights cause (used to size the fp8 tolerance)
  */
 int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                      const double *q, const double *k, const double *v, int kv_cap,
@@ -177,7 +201,8 @@ int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                      int causal, int window, int rowdrop, uint32_t seed, uint32_t threshold,
                      const double *add_mask, int64_t mask_ld, const int32_t *lens,
                      const uint8_t *block_mask, int64_t bm_sb, int64_t bm_sh, int64_t bm_sq,
-                     const int64_t *rows, int64_t nrows, double *out, double *lse)
+                     const int64_t *rows, int64_t nrows, double *out, double *lse,
+                     double *wsq, double *wvar)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return -1;
     if (Hq % Hkv != 0 || kv_cap < Skv) return -1;
@@ -206,7 +231,8 @@ int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                 const int i = (int)(r % Sq);
                 const int h = (int)((r / Sq) % Hq);
                 const int b = (int)(r / ((int64_t)Sq * Hq));
-                attend_row(&p, b, h, i, s, out + n * D, lse + n);
+                attend_row(&p, b, h, i, s, out + n * D, lse + n, wsq ? wsq + n : NULL,
+                           wvar ? wvar + n * D : NULL);
             }
         }
         free(s);

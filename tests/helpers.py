@@ -40,6 +40,9 @@ def assert_parity(got, ref, atol, rtol, what=""):
                              f"got {got[bad_nf][:4]} want {ref[bad_nf][:4]}"
     assert np.isfinite(got[fin]).all(), f"{what}: non-finite output where the reference is finite"
     err = np.abs(got[fin] - ref[fin])
+    # atol / rtol may be scalars or per-element arrays shaped like ref
+    atol = np.broadcast_to(np.asarray(atol, dtype=np.float64), ref.shape)[fin]
+    rtol = np.broadcast_to(np.asarray(rtol, dtype=np.float64), ref.shape)[fin]
     lim = atol + rtol * np.abs(ref[fin])
     ok = err <= lim
     if not ok.all():

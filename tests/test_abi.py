@@ -159,3 +159,17 @@ def test_block_mask_create_rejects_before_launch(args, status):
     lib = mm.load_library()
     fl, w, sq, skv, out, ld = args
     assert lib.mm_block_mask_create(fl, w, sq, skv, out, ld, None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3, descale_q=1.0, descale_k=1.0, descale_v=1.0, q_strides=mm._I64x3(4 * 16 * 128, 16 * 128, 136)), STRIDE),
+    (dict(dtype=3, descale_q=0.0, descale_k=1.0, descale_v=1.0), SHAPE),
+    (dict(dtype=3, descale_q=1.0, descale_k=float("nan"), descale_v=1.0), SHAPE),
+    (dict(dtype=3, descale_q=1.0, descale_k=1.0, descale_v=-2.0), SHAPE),
+    (dict(dtype=3, descale_q=1.0, descale_k=1.0, descale_v=1.0, Sq=0), OK),
+    # 16-bit inputs ignore the descale fields: with zeros there the call still gets as
+    # far as the stride check (a bad stride keeps it on the host)
+    (dict(dtype=2, descale_q=0.0, q_strides=mm._I64x3(-1, 0, 0)), STRIDE),
+])
+def test_fp8_args_rejected_before_launch(kw, status):
+    assert _fwd(**kw) == status

@@ -535,3 +535,45 @@ def test_block_classes_leave_attention_unchanged(Sq, Skv, causal, window):
     O1, L1 = oracle.attention(q, k, v, scale=0.3, causal=causal, window=window, block_mask=c)
     np.testing.assert_array_equal(L0, L1)
     np.testing.assert_array_equal(O0, O1)
+
+
+# ------------------------------------------------ weight sensitivity (sizes the fp8 tolerance)
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 4)])
+def test_sensitivity_vs_brute_force(causal, window):
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 19, 23, 8
+    x = inputs.attention_inputs(21, B, Hq, Hkv, Sq, Skv, D, "f32")
+    q, k, v = (_f64(x[n], "f32") for n in ("q", "k", "v"))
+    O, L, wsq, wvar = oracle.attention(q, k, v, scale=0.4, causal=causal, window=window,
+                                       sensitivity=True)
+    # weights by brute force: w = exp(S - LSE) over the kept keys
+    vv = np.repeat(v, Hq // Hkv, axis=1)
+    S = 0.4 * np.matmul(q, np.swapaxes(np.repeat(k, Hq // Hkv, axis=1), -1, -2))
+    i, j = np.arange(Sq)[:, None], np.arange(Skv)[None, :]
+    keep = np.ones((Sq, Skv), dtype=bool)
+    if causal:
+        keep &= j <= i
+    if window is not None:
+        keep &= np.abs(i - j) <= window
+    S = np.where(keep, S, -np.inf)
+    W = np.exp(S - logsumexp(S, axis=-1, keepdims=True))
+    Ob = np.matmul(W, vv)
+    close(O, Ob, 1e-11)
+    close(wsq, (W ** 2).sum(-1), 1e-11)
+    dv = vv[:, :, None, :, :] - Ob[:, :, :, None, :]          # [B,H,Sq,Skv,D]
+    close(wvar, np.einsum("bhij,bhijd->bhid", W ** 2, dv ** 2), 1e-11)
+
+
+def test_sensitivity_closed_form_uniform_weights():
+    """Q = 0: n equal weights, so wsq = 1/n and wvar = (population variance of V) / n."""
+    q, k, v = _zero_q(1, 2, 2, 3, 9, 4)
+    O, L, wsq, wvar = oracle.attention(q, k, v, scale=1.0, sensitivity=True)
+    close(wsq, np.full(wsq.shape, 1 / 9))
+    want = v.var(axis=2, keepdims=True) / 9  # numpy var is the population variance
+    close(wvar, np.broadcast_to(want, wvar.shape))
+
+
+def test_sensitivity_fully_masked_rows_are_zero():
+    q, k, v = _rand(1, 2, 2, 200, 10, 8)
+    _, L, wsq, wvar = oracle.attention(q, k, v, scale=0.3, causal=True, window=3, sensitivity=True)
+    dead = ~np.isfinite(L)
+    assert dead.any() and np.all(wsq[dead] == 0) and np.all(wvar[dead] == 0)
