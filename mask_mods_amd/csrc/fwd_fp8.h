@@ -38,7 +38,10 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // two e4m3 values (round to nearest even) into the low or high half of a word
-__device__ __forceinline__ int pack_fp8_lo(float a, float b) { return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false); }
+// (the low-half write keeps the high half of `a`'s register, which pack_fp8_hi replaces)
+__device__ __forceinline__ int pack_fp8_lo(float a, float b) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
+}
 __device__ __forceinline__ int pack_fp8_hi(float a, float b, int w) { return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, true); }
 
 // Swizzled row-major tile of D one-byte elements per key.
@@ -68,10 +71,10 @@ void fwd_fp8_kernel(FwdParams p) {
     constexpr float kRescale = 8.f;
     static_assert(NL >= 1 && NL * NW == 2 * KBLK && KBLK % NL == 0, "tile shape");
 
+    // three stages, each a K tile then a V tile
     __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
     __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
-    unsigned char *const KB[2] = {kv0, kv1};
-    unsigned char *const VB[2] = {kv0 + TILEB, kv1 + TILEB};
+    __shared__ __attribute__((aligned(1024))) unsigned char kv2[2 * TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -89,7 +92,10 @@ void fwd_fp8_kernel(FwdParams p) {
     const uint8_t *kg = (const uint8_t *)p.k + b * p.k_sb + hk * p.k_sh;
     const uint8_t *vg = (const uint8_t *)p.v + b * p.v_sb + hk * p.v_sh;
 
-    const int r0 = q0 + wave * 32;
+    // the wave index as a scalar: tile classifications derived from it are wave-uniform
+    // branches, not per-lane masked code
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int r0 = q0 + wave_s * 32;  // first row of this wave
     const int row = r0 + l32;
 
     // Q^T fragments (B operand): row `row`, dims 64*c + 32*hi .. +31
@@ -138,7 +144,6 @@ void fwd_fp8_kernel(FwdParams p) {
     }
 
     // copies: wave w moves blocks w*NL .. +NL-1 of the tile pair (K blocks first, then V)
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const bool cp_v = wave_s * NL >= KBLK;
     const int blk0 = wave_s * NL - (cp_v ? KBLK : 0);
     const uint8_t *cp_src = cp_v ? vg : kg;
@@ -177,77 +182,80 @@ void fwd_fp8_kernel(FwdParams p) {
     const int one4 = 0x38383838;  // four e4m3 ones
     const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
 
-    auto tile = [&](int kt, int blk, const unsigned char *Kt, const unsigned char *Vt, int next,
-                    unsigned char *Kn) {
-        if (next >= 0) load_tile(next, Kn);
+    // ---- the four phases of a tile ----
+    // S^T of the tile in stage Kt (raw dot products)
+    auto qk = [&](const unsigned char *Kt, f32x16 (&sacc)[NKB]) {
+        u32x4 ka[NKB][NC][2];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) ka[kb][c][e] = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[c][e]);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            sacc[kb] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 x0 = ka[kb][c][0], x1 = ka[kb][c][1];
+                const i32x8 a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                 (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                sacc[kb] = mfma_fp8(a, qf[c], sacc[kb]);
+            }
+        }
+    };
+    // scale / score_mod / mask_mod where the tile needs them; returns the multiplier the
+    // exponent (and the max) apply to sacc: 1 when sacc was rewritten as base-2 scores,
+    // else the scale (plain tiles keep the raw dot products)
+    auto transform = [&](int kt, int blk, f32x16 (&sacc)[NKB]) -> float {
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
         const bool pred = blk == 1;
-        bool skip = kt >= kt_hi, need_mask = k0 + BN > p.Skv;
+        bool dead = false, need_mask = k0 + BN > p.Skv;
         if ((MASK & MASK_CAUSAL) && pred) {
-            skip |= k0 > r_last;
+            dead |= k0 > r_last;
             need_mask |= k0 + BN - 1 > r0;
         }
         if ((MASK & MASK_WINDOW) && pred) {
-            skip |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
+            dead |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
-        if (skip) return;
-
-        f32x16 sacc[NKB];
-        {
-            u32x4 ka[NKB][NC][2];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-#pragma unroll
-                    for (int e = 0; e < 2; ++e)
-                        ka[kb][c][e] = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[c][e]);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                sacc[kb] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const u32x4 x0 = ka[kb][c][0], x1 = ka[kb][c][1];
-                    const i32x8 a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-                    sacc[kb] = mfma_fp8(a, qf[c], sacc[kb]);
-                }
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, NKB * NC * 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, NKB * NC, 0);
-        }
-        float mloc = -INFINITY, cc;
-        const bool general = ALIBI || need_mask || !(c2 > 0.f);
-        if (general) {
-            const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
+        if (!(ALIBI || need_mask || !(c2 > 0.f))) return c2;
+        const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
+        auto scores = [&](bool masked) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
                     float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
-                    if (need_mask) {
+                    if (masked) {
                         const int j = k0 + 4 * hi + jo;
-                        bool keep = j < p.Skv;
+                        bool keep = (j < p.Skv) & !dead;
                         if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
                         if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
                         t = keep ? t : -INFINITY;
                     }
                     sacc[kb][e] = t;
-                    mloc = fmaxf(mloc, t);
                 }
             }
-            cc = 1.f;
-        } else {
+        };
+        // one uniform branch, then straight-line code for the whole tile
+        if (need_mask) scores(true);
+        else scores(false);
+        return 1.f;
+    };
+    // the tile's row max (in base-2 units) over both lane halves
+    auto tile_max = [&](const f32x16 (&sacc)[NKB], float cc) -> float {
+        float m = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
-            mloc *= c2;
-            cc = c2;
-        }
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, sacc[kb][e]);
+        return m * cc;
+    };
+    // lazy rescale: raise the running max only when the tile exceeds it by > 2^8
+    auto rescale = [&](float mloc) {
         mloc = row_max2(mloc);
         if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescale)) {
             const float m_new = fmaxf(m_run, mloc);
@@ -257,10 +265,11 @@ void fwd_fp8_kernel(FwdParams p) {
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             m_run = m_new;
         }
+    };
+    // P = 2^(t - m) rounded to e4m3; byte i of the operand is accumulator element i % 16
+    // of key block i / 16
+    auto expcvt = [&](const f32x16 (&sacc)[NKB], float cc, int (&pp)[8]) {
         const float nm = m_run == -INFINITY ? 0.f : -m_run;
-        // P = 2^(t - m) rounded to e4m3; byte i of the operand is accumulator element
-        // i % 16 of key block i / 16
-        int pp[8];
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const int kb = w >> 2, e0 = 4 * (w & 3);
@@ -270,58 +279,111 @@ void fwd_fp8_kernel(FwdParams p) {
             const float x3 = fast_exp2(fmaf(sacc[kb][e0 + 3], cc, nm));
             pp[w] = pack_fp8_hi(x2, x3, pack_fp8_lo(x0, x1));
         }
+    };
+    // O^T += V^T P^T (the row sum, ones x P, is issued with the products of S)
+    auto pv = [&](const unsigned char *Vt, const int (&pp)[8]) {
         const i32x8 pf = {pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
-        {
-            i32x2 va[DB][4];
+        i32x2 va[DB][4];
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    va[db][r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (MM_LDS i32x2 *)(Vt + voff[db] + 16 * r * TL::ROWB));
-            lacc = mfma_fp8(ones, pf, lacc);
+            for (int r = 0; r < 4; ++r)
+                va[db][r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MM_LDS i32x2 *)(Vt + voff[db] + 16 * r * TL::ROWB));
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const i32x8 a = {va[db][0][0], va[db][0][1], va[db][1][0], va[db][1][1],
-                                 va[db][2][0], va[db][2][1], va[db][3][0], va[db][3][1]};
-                oacc[db] = mfma_fp8(a, pf, oacc[db]);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, DB + 1, 1);
+        for (int db = 0; db < DB; ++db) {
+            const i32x8 a = {va[db][0][0], va[db][0][1], va[db][1][0], va[db][1][1],
+                             va[db][2][0], va[db][2][1], va[db][3][0], va[db][3][1]};
+            oacc[db] = mfma_fp8(a, pf, oacc[db]);
         }
     };
 
-    if (MASK & MASK_BLOCK) {
-        BlockWalk walk(p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)qt * p.bm_sq, kt_hi);
-        const int nkb = kt_hi;
-        int cv, nv;
-        int cur = walk.next(0, lane, cv);
-        int nxt = cur < nkb ? walk.next(cur + 1, lane, nv) : nkb;
-        if (cur < nkb) load_tile(cur, KB[0]);
-        kv_barrier<0>();
-        while (cur < nkb) {
-            tile(cur, cv, KB[0], VB[0], nxt < nkb ? nxt : -1, KB[1]);
-            kv_barrier<0>();
-            cur = nxt;
-            cv = nv;
-            if (cur >= nkb) break;
-            nxt = walk.next(cur + 1, lane, nv);
-            tile(cur, cv, KB[1], VB[1], nxt < nkb ? nxt : -1, KB[0]);
-            kv_barrier<0>();
-            cur = nxt;
-            cv = nv;
-            if (cur < nkb) nxt = walk.next(cur + 1, lane, nv);
+    // ---- software pipeline over the visited tiles t_0, t_1, ... ----
+    // Iteration n copies t_{n+2} into the free stage, computes S of t_{n+1} on the MFMA
+    // while the VALU turns S of t_n into P, then runs P V of t_n while the VALU scales,
+    // masks and reduces S of t_{n+1}. Three LDS stages hold t_n (its V), t_{n+1} (its K)
+    // and the copy in flight. The MFMAs of t_{n+1} are issued even past the last tile
+    // (on stale data, results unused) so the iteration stays one straight-line block.
+    constexpr int END = 1 << 30;
+    BlockWalk walk((MASK & MASK_BLOCK) ? p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)qt * p.bm_sq : nullptr,
+                   kt_hi);
+    auto next_tile = [&](int t, int &cls) -> int {
+        if (t >= END) { cls = 0; return END; }
+        if (MASK & MASK_BLOCK) {
+            const int n = walk.next(t + 1, lane, cls);
+            return n < kt_hi ? n : END;
         }
+        cls = 1;
+        return t + 1 < kt_hi ? t + 1 : END;
+    };
+    int c_cur, c_nxt, c_aft;
+    int cur;
+    if (MASK & MASK_BLOCK) {
+        cur = walk.next(0, lane, c_cur);
+        if (cur >= kt_hi) cur = END;
     } else {
-        if (kt_lo < kt_hi) load_tile(kt_lo, KB[0]);
+        cur = kt_lo < kt_hi ? kt_lo : END;
+        c_cur = 1;
+    }
+    if (cur < END) {
+        int nxt = next_tile(cur, c_nxt);
+        int aft = next_tile(nxt, c_aft);
+        load_tile(cur, kv0);
+        load_tile(nxt < END ? nxt : cur, kv1);
         kv_barrier<0>();
-        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-            tile(kt, 1, KB[0], VB[0], kt + 1 < kt_hi ? kt + 1 : -1, KB[1]);
-            kv_barrier<0>();
-            if (kt + 1 < kt_hi) {
-                tile(kt + 1, 1, KB[1], VB[1], kt + 2 < kt_hi ? kt + 2 : -1, KB[0]);
-                kv_barrier<0>();
+        f32x16 s_cur[NKB];
+        qk(kv0, s_cur);
+        float cc_cur = transform(cur, c_cur, s_cur);
+        rescale(tile_max(s_cur, cc_cur));
+        auto body = [&](unsigned char *Sc, unsigned char *Sn, unsigned char *Sa) {
+            load_tile(aft < END ? aft : cur, Sa);
+            f32x16 s_nxt[NKB];
+            qk(Sn, s_nxt);
+            int pp[8];
+            expcvt(s_cur, cc_cur, pp);
+            lacc = mfma_fp8(ones, i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]}, lacc);
+            // interleave: the K reads first, then each MFMA of S(t_{n+1}) followed by a
+            // share of the exponentials of t_n
+            __builtin_amdgcn_sched_group_barrier(0x100, NKB * NC * 2, 0);
+#pragma unroll
+            for (int i = 0; i < NKB * NC; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            const float cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, s_nxt);
+            pv(Sc + TILEB, pp);
+            const float mloc = tile_max(s_nxt, cc_nxt);
+            // then the V reads, and each MFMA of P V followed by a share of the max
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);
+#pragma unroll
+            for (int i = 0; i < DB + 1; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+            // a tile past the end must not move the running max
+            rescale(nxt < END ? mloc : -INFINITY);
+            kv_barrier<0>();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
+            cc_cur = cc_nxt;
+        };
+        auto advance = [&]() {
+            cur = nxt;
+            c_cur = c_nxt;
+            nxt = aft;
+            c_nxt = c_aft;
+            aft = next_tile(aft, c_aft);
+        };
+        for (;;) {
+            body(kv0, kv1, kv2);
+            if (nxt >= END) break;
+            advance();
+            body(kv1, kv2, kv0);
+            if (nxt >= END) break;
+            advance();
+            body(kv2, kv0, kv1);
+            if (nxt >= END) break;
+            advance();
         }
     }
 

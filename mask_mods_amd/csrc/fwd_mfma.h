@@ -109,7 +109,10 @@ void fwd_mfma_kernel(FwdParams p) {
     const uint16_t *kg = (const uint16_t *)p.k + b * p.k_sb + hk * p.k_sh;
     const uint16_t *vg = (const uint16_t *)p.v + b * p.v_sb + hk * p.v_sh;
 
-    const int r0 = q0 + wave * 32;  // first row of this wave
+    // the wave index as a scalar: tile classifications derived from it are wave-uniform
+    // branches, not per-lane masked code
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int r0 = q0 + wave_s * 32;  // first row of this wave
     const int row = r0 + l32;       // the row this lane owns
 
     // Q^T fragments (B operand): row `row`, dims 16*ks + 8*hi .. +7
@@ -168,7 +171,6 @@ void fwd_mfma_kernel(FwdParams p) {
     // 64*stride); full tiles add a wave-uniform base so the copy uses the
     // scalar-base + vector-offset address form. The tile that crosses Skv clamps rows
     // to the last key instead (their scores are masked).
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     uint32_t kgo[LOADS], vgo[LOADS];
     int trow[LOADS], tchunk[LOADS];
 #pragma unroll
