@@ -37,7 +37,9 @@ FWD = dict(B=2, H=32, S=8192, D=128)
 DEC = dict(B=1, H=32, L=32768, D=128)
 FWD_KERNEL = "fwd_mfma_kernel"
 DEC_KERNELS = ("decode_split_kernel", "decode_merge_kernel")
-KERNEL_SOURCES = ["mask_mods_amd/csrc/fwd_mfma.h", "mask_mods_amd/csrc/common.h",
+FP8_KERNEL = "fwd_fp8_kernel"
+KERNEL_SOURCES = ["mask_mods_amd/csrc/fwd_mfma.h", "mask_mods_amd/csrc/fwd_fp8.h",
+                  "mask_mods_amd/csrc/fwd_common.h", "mask_mods_amd/csrc/common.h",
                   "mask_mods_amd/csrc/decode.hip", "mask_mods_amd/csrc/kernels.h"]
 
 
@@ -56,6 +58,11 @@ def fwd_flops(B, H, Sq, Skv, D, causal=False):
 
 def fwd_bytes(B, H, S, D, elt=2):
     return 4 * B * H * S * D * elt + B * H * S * 4
+
+
+def fp8_bytes(B, H, S, D):
+    """Q, K, V in one byte per element, O in bf16, LSE in fp32: each moved once."""
+    return 3 * B * H * S * D + 2 * B * H * S * D + 4 * B * H * S
 
 
 def dec_bytes(B, H, L, D, elt=2):
@@ -153,6 +160,7 @@ def ingest(root):
     for name, sub, match, alg in [
         (FWD_KERNEL, "fwd", lambda k: FWD_KERNEL in k, fwd_bytes(FWD["B"], FWD["H"], FWD["S"], FWD["D"])),
         ("decode", "decode", lambda k: "decode_" in k, dec_bytes(DEC["B"], DEC["H"], DEC["L"], DEC["D"])),
+        (FP8_KERNEL, "fp8", lambda k: FP8_KERNEL in k, fp8_bytes(FWD["B"], FWD["H"], FWD["S"], FWD["D"])),
     ]:
         fr = _read_counters(_find(root, "fetch_" + sub, "counter_collection.csv"))
         wr = _read_counters(_find(root, "write_" + sub, "counter_collection.csv"))
@@ -167,6 +175,12 @@ def ingest(root):
     print(json.dumps(res, indent=1))
 
 
+def to_fp8(t, torch):
+    """Per-tensor e4m3 quantisation on the device: (t / s) rounded, s = max|t| / 448."""
+    s = (t.float().abs().max() / 448.0).item()
+    return (t.float() / s).to(torch.float8_e4m3fn), s
+
+
 def profile_one(args, torch, mm, inputs, dev):
     """Run one kernel family only (for rocprofv3 passes); prints a small JSON line."""
     def dev_tensor(bits, dtype):
@@ -179,6 +193,16 @@ def profile_one(args, torch, mm, inputs, dev):
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)
         unit_bytes = 2 * n
+    elif args.only == "fp8":
+        B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
+        (q8, sq), (k8, sk), (v8, sv) = (to_fp8(t, torch) for t in (q, k, v))
+        out = torch.empty_like(q)
+        lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        fn = lambda: mm.attn_fwd(q8, k8, v8, scale, descale=(sq, sk, sv), out=out, lse=lse)
+        unit_bytes = fp8_bytes(B, H, S, D)
     elif args.only == "fwd":
         B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
         x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
@@ -218,7 +242,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fp8", "decode", "copy"], default=None,
                     help="profiling aid: run just one kernel family (or a plain 1 GiB device copy "
                          "used to calibrate the HBM byte counters) and print its timing")
     ap.add_argument("--ingest", metavar="DIR", default=None,
@@ -319,10 +343,7 @@ def main():
         specs["block_sparse_50"] = dict(block_mask=bm_rand)
         block_pairs = int((bm_rand_np != 0).sum()) * mm.BLOCK_Q * mm.BLOCK_KV
         # fp8 (e4m3) inputs: the same draws quantised per tensor on the device
-        def to_fp8(t):
-            s = (t.float().abs().max() / 448.0).item()
-            return (t.float() / s).to(torch.float8_e4m3fn), s
-        (q8, sq), (k8, sk), (v8, sv) = to_fp8(q), to_fp8(k), to_fp8(v)
+        (q8, sq), (k8, sk), (v8, sv) = (to_fp8(t, torch) for t in (q, k, v))
         fp8_kw = dict(q=q8, k=k8, v=v8, descale=(sq, sk, sv))
         specs["fp8_no_mod"] = dict(fp8_kw)
         specs["fp8_causal"] = dict(fp8_kw, causal=True)
@@ -391,6 +412,16 @@ def main():
         },
         "cases_s8192": cases,
     }
+    if "fp8_no_mod" in cases:
+        c8 = cases["fp8_no_mod"]
+        a8 = fwd_flops(B, H, S, S, D) / (c8["us"] * 1e-6) / 1e12
+        res["fp8"] = {
+            "value": round(a8, 1), "unit": "TFLOP/s", "us": c8["us"],
+            "roofline": {"bound": "mfma", "achieved": round(a8, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(a8 / MFMA_FP8_PEAK_TFLOPS, 4),
+                         "traffic": load_traffic(FP8_KERNEL), "kernel": FP8_KERNEL,
+                         "algorithmic": "4*B*H*S*S*D flop per launch; e4m3 Q/K/V, bf16 O"},
+        }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(xf, args.cpu_seconds)
     print(json.dumps(res), flush=True)

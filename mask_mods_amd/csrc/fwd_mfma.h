@@ -60,8 +60,14 @@ template <int D>
 struct Tile {
     static constexpr int ROWB = 2 * D;  // bytes per key row
     static constexpr int CH = D / 8;    // 16-byte chunks per row
+    // The K reads hit 16 consecutive rows at one chunk, so swz must be a bijection on
+    // the row index modulo 16 (D = 128; for D = 64, two rows share a 256-byte bank
+    // window and swz of rows of equal parity must differ). The transposed V reads of a
+    // half-wave hit 4 consecutive rows (4a .. 4a+3) x 4 consecutive chunks, so the high
+    // bits of swz must differ across such rows: row 4a+b takes b in bits 2-3 (D = 128),
+    // and rows 4a, 4a+2 differ in bit 2 (D = 64).
     __host__ __device__ static constexpr int swz(int r) {
-        return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((r >> 1) & 7);
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
     }
     __host__ __device__ static constexpr int off(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
 };
