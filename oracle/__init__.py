@@ -54,6 +54,15 @@ def load():
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_threads.restype = None
+    lib.oracle_attention_bwd.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _dp, _dp, _dp, _dp,
+        ctypes.c_double, ctypes.c_int, _dp,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
+        _bp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        _dp, _dp, _dp,
+    ]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
     lib.oracle_attention.argtypes = [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         _dp, _dp, _dp, ctypes.c_int,
@@ -184,3 +193,39 @@ def block_classes(Sq: int, Skv: int, *, causal: bool = False, window=None) -> np
                 keep &= np.abs(ii - jj) <= window
             out[qb, kb] = 2 if keep.all() else (1 if keep.any() else 0)
     return out
+
+
+def attention_bwd(q, k, v, dout, *, scale, causal=False, window=None, alibi=False, slopes=None,
+                  rowdrop=None, block_mask=None):
+    """Gradients (dq, dk, dv) of sum(dout * O) for the forward of ``attention`` (no
+    additive mask or lengths), in float64. Shapes as ``attention`` with kv_cap = Skv."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    assert v.shape == k.shape and dout.shape == q.shape
+    if slopes is not None:
+        slopes = np.ascontiguousarray(slopes, dtype=np.float64)
+    seed, thr = (0, 0) if rowdrop is None else rowdrop
+    bm_s = (0, 0, 0)
+    if block_mask is not None:
+        block_mask = np.ascontiguousarray(block_mask, dtype=np.uint8)
+        Bb, Hb, nqb, nkb = block_mask.shape
+        assert Bb in (1, B) and Hb in (1, Hq)
+        assert nqb >= -(-Sq // BLOCK_Q) and nkb >= -(-Skv // BLOCK_KV)
+        bm_s = (0 if Bb == 1 else Hb * nqb * nkb, 0 if Hb == 1 else nqb * nkb, nkb)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rc = load().oracle_attention_bwd(
+        B, Hq, Hkv, Sq, Skv, D, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(dout, _dp),
+        float(scale), int(bool(alibi)), _ptr(slopes, _dp),
+        int(bool(causal)), -1 if window is None else int(window), int(rowdrop is not None),
+        seed & 0xFFFFFFFF, thr & 0xFFFFFFFF,
+        _ptr(block_mask, _bp), bm_s[0], bm_s[1], bm_s[2],
+        _ptr(dq, _dp), _ptr(dk, _dp), _ptr(dv, _dp))
+    if rc != 0:
+        raise ValueError("oracle_attention_bwd rejected its arguments")
+    return dq, dk, dv

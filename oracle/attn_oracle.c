@@ -40,6 +40,9 @@
  * FlyDSL PR's named future phase (block sparsity), read as PyTorch's BlockMask with
  * its full / partial block lists.
  *
+ * Backward (oracle_attention_bwd): the gradients of sum(dO * O) with respect to q, k, v
+ * written out from the softmax Jacobian, over the same scores (below).
+ *
  * Inputs are float64 arrays holding the exact values of the bf16/f16/f32 inputs.
  * Nothing here is blocked, fused, reordered or rounded beyond that definition.
  */
@@ -107,17 +110,15 @@ typedef struct {
 #define ORACLE_BLOCK_Q 128
 #define ORACLE_BLOCK_KV 64
 
-/* One query row. s: scratch of Skv doubles. o: D outputs. wsq, wvar: NULL or the
- * row's first-order sensitivity to relative perturbations of the weights (below). */
-static void attend_row(const problem *p, int b, int h, int i, double *s, double *o, double *lse,
-                       double *wsq, double *wvar)
+/* The final scores of one query row: s[j] = scale*q.k (+ alibi) (+ additive mask), or
+ * -inf where the mask_mods / block mask / length drop the pair. Returns their max. */
+static double row_scores(const problem *p, int b, int h, int i, double *s)
 {
     const int group = p->Hq / p->Hkv;
     const int hk = h / group;
     const int64_t row = ((int64_t)b * p->Hq + h) * p->Sq + i;
     const double *qi = p->q + row * p->D;
     const double *kb = p->k + ((int64_t)b * p->Hkv + hk) * p->kv_cap * p->D;
-    const double *vb = p->v + ((int64_t)b * p->Hkv + hk) * p->kv_cap * p->D;
     const int len = p->lens ? p->lens[b] : p->Skv;
     const int dropped = p->rowdrop && oracle_row_dropped(p->seed, p->threshold, row);
     const double slope = p->alibi ? (p->slopes ? p->slopes[h] : oracle_alibi_slope(h, p->Hq)) : 0.0;
@@ -146,6 +147,17 @@ static void attend_row(const problem *p, int b, int h, int i, double *s, double 
         s[j] = x;
         if (x > M) M = x;
     }
+    return M;
+}
+
+/* One query row. s: scratch of Skv doubles. o: D outputs. wsq, wvar: NULL or the
+ * row's first-order sensitivity to relative perturbations of the weights (below). */
+static void attend_row(const problem *p, int b, int h, int i, double *s, double *o, double *lse,
+                       double *wsq, double *wvar)
+{
+    const int hk = h / (p->Hq / p->Hkv);
+    const double *vb = p->v + ((int64_t)b * p->Hkv + hk) * p->kv_cap * p->D;
+    const double M = row_scores(p, b, h, i, s);
     for (int d = 0; d < p->D; ++d) o[d] = 0.0;
     if (wsq) *wsq = 0.0;
     if (wvar)
@@ -236,6 +248,92 @@ int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
             }
         }
         free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Gradients of the forward above (no additive mask, no lengths) with respect to q, k, v
+ * for an upstream gradient dO, from the definition: with P_ij = exp(s_ij - LSE_i) over
+ * the kept pairs and O_i = sum_j P_ij V_j,
+ *   dV_j = sum_i P_ij dO_i
+ *   dP_ij = dO_i . V_j,   D_i = dO_i . O_i = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)                (softmax Jacobian)
+ *   dQ_i = scale * sum_j dS_ij K_j,  dK_j = scale * sum_i dS_ij Q_i
+ * The alibi bias and the masks do not depend on q, k, v: masked pairs have P = 0 and
+ * contribute nothing; fully masked (and dropped) rows give zero gradients. With GQA the
+ * K/V gradients of a kv head sum over the query heads that read it.
+ * Layouts as oracle_attention (k, v, dk, dv with kv_cap = Skv). Parallel over (b, kv
+ * head), so each K/V gradient has one writer. Returns 0, or -1 on invalid arguments.
+ */
+int oracle_attention_bwd(int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                         const double *q, const double *k, const double *v, const double *dout,
+                         double scale, int alibi, const double *slopes,
+                         int causal, int window, int rowdrop, uint32_t seed, uint32_t threshold,
+                         const uint8_t *block_mask, int64_t bm_sb, int64_t bm_sh, int64_t bm_sq,
+                         double *dq, double *dk, double *dv)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return -1;
+    if (Hq % Hkv != 0) return -1;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    problem p = {B, Hq, Hkv, Sq, Skv, D, Skv, q, k, v, scale, alibi, slopes,
+                 causal, window, rowdrop, seed, threshold, NULL, 0, NULL,
+                 block_mask, bm_sb, bm_sh, bm_sq};
+    const int group = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !o) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
+                const int b = (int)(bk / Hkv), hk = (int)(bk % Hkv);
+                const double *kb = k + bk * Skv * D, *vb = v + bk * Skv * D;
+                double *dkb = dk + bk * Skv * D, *dvb = dv + bk * Skv * D;
+                for (int64_t t = 0; t < (int64_t)Skv * D; ++t) dkb[t] = dvb[t] = 0.0;
+                for (int h = hk * group; h < (hk + 1) * group; ++h) {
+                    for (int i = 0; i < Sq; ++i) {
+                        const int64_t row = ((int64_t)b * Hq + h) * Sq + i;
+                        const double *qi = q + row * D, *doi = dout + row * D;
+                        double *dqi = dq + row * D;
+                        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+                        const double M = row_scores(&p, b, h, i, s);
+                        if (M == -INFINITY) continue;
+                        double Lsum = 0.0;
+                        for (int j = 0; j < Skv; ++j)
+                            if (s[j] != -INFINITY) Lsum += exp(s[j] - M);
+                        const double lse = M + log(Lsum);
+                        /* O_i and D_i */
+                        for (int d = 0; d < D; ++d) o[d] = 0.0;
+                        for (int j = 0; j < Skv; ++j) {
+                            if (s[j] == -INFINITY) continue;
+                            const double pij = exp(s[j] - lse);
+                            for (int d = 0; d < D; ++d) o[d] += pij * vb[(int64_t)j * D + d];
+                        }
+                        double Di = 0.0;
+                        for (int d = 0; d < D; ++d) Di += doi[d] * o[d];
+                        for (int j = 0; j < Skv; ++j) {
+                            if (s[j] == -INFINITY) continue;
+                            const double pij = exp(s[j] - lse);
+                            double dpij = 0.0;
+                            for (int d = 0; d < D; ++d) dpij += doi[d] * vb[(int64_t)j * D + d];
+                            const double dsij = pij * (dpij - Di);
+                            for (int d = 0; d < D; ++d) {
+                                dvb[(int64_t)j * D + d] += pij * doi[d];
+                                dqi[d] += scale * dsij * kb[(int64_t)j * D + d];
+                                dkb[(int64_t)j * D + d] += scale * dsij * qi[d];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(s);
+        free(o);
     }
     return bad ? -1 : 0;
 }

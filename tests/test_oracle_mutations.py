@@ -37,6 +37,39 @@ MUTANTS = {
 }
 
 
+# mistakes in the backward, caught by the backward's pins (test_oracle_bwd.py)
+MUTANTS_BWD = {
+    "bwd_no_row_term": ("const double dsij = pij * (dpij - Di);", "const double dsij = pij * dpij;"),
+    "bwd_dk_unscaled": ("dkb[(int64_t)j * D + d] += scale * dsij * qi[d];",
+                        "dkb[(int64_t)j * D + d] += dsij * qi[d];"),
+    "bwd_dv_from_ds": ("dvb[(int64_t)j * D + d] += pij * doi[d];", "dvb[(int64_t)j * D + d] += dsij * doi[d];"),
+    "bwd_dq_from_v": ("dqi[d] += scale * dsij * kb[(int64_t)j * D + d];",
+                      "dqi[d] += scale * dsij * vb[(int64_t)j * D + d];"),
+    "bwd_group_one_head": ("for (int h = hk * group; h < (hk + 1) * group; ++h) {",
+                           "for (int h = hk * group; h < hk * group + 1; ++h) {"),
+}
+
+
+def _run_mutant(name, before, after, tmp_path, test_file):
+    src = open(SRC).read()
+    assert src.count(before) == 1, name
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(src.replace(before, after))
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           str(c), "-o", str(so), "-lm"])
+    env = dict(os.environ, MASKMODS_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", test_file)],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the pins of {test_file}:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_BWD))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    _run_mutant(name, *MUTANTS_BWD[name], tmp_path, "test_oracle_bwd.py")
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     before, after = MUTANTS[name]
