@@ -151,8 +151,41 @@ typedef struct mm_decode_args {
     int32_t num_splits;      /* 0 = automatic; else the KV split count to use         */
 } mm_decode_args;
 
+typedef struct mm_bwd_args {
+    const void *q, *k, *v;   /* the forward's inputs (as mm_fwd_args)                    */
+    const void *out;         /* the forward's O [B, Hq, Sq, D]                           */
+    const void *dout;        /* upstream gradient dO [B, Hq, Sq, D]                      */
+    const float *lse;        /* the forward's LSE, fp32 contiguous [B, Hq, Sq] (required)*/
+    void *dq;                /* [B, Hq, Sq, D]  outputs, dtype of the inputs             */
+    void *dk;                /* [B, Hkv, Skv, D]                                         */
+    void *dv;                /* [B, Hkv, Skv, D]                                         */
+    int32_t dtype;           /* MM_BF16 or MM_F16                                         */
+    int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128}                                    */
+    int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3], do_strides[3];
+    int64_t dq_strides[3], dk_strides[3], dv_strides[3]; /* elements, for b, h, s        */
+    float scale;             /* the forward's scale                                       */
+    int32_t causal;          /* the forward's causal flag                                 */
+    mm_mods mods;            /* the forward's mods (score_mod, mask_mods, block mask)     */
+    void *workspace;         /* device scratch, >= mm_attn_bwd_workspace_size()           */
+    size_t workspace_bytes;
+} mm_bwd_args;
+
 /* Forward attention. Returns MM_OK or a negative mm_status. */
 mm_status mm_attn_fwd(const mm_fwd_args *args, void *stream);
+
+/* Bytes of device workspace mm_attn_bwd needs (0 if invalid). */
+size_t mm_attn_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Sq);
+
+/* Backward of mm_attn_fwd: the gradients of sum(dout * out) with respect to q, k and v,
+ * for the same mods (the alibi bias, the mask_mods and the block mask do not depend on
+ * q, k, v; masked pairs and rows with no kept key, LSE = -inf, contribute nothing;
+ * with GQA the K/V gradients sum over the query heads of a group). Written from the
+ * softmax Jacobian as in the FlyDSL PR's named future phase (backward): with
+ * P = exp(s - LSE), dV = P^T dO, dS = P (dO V^T - rowsum(dO * O)), dQ = scale dS K,
+ * dK = scale dS^T Q. P and dS are rounded to the input dtype for their products;
+ * accumulation is fp32. Three launches on `stream` (a pre-pass into the workspace,
+ * then dQ, then dK/dV); dq, dk, dv are written, not accumulated into. */
+mm_status mm_attn_bwd(const mm_bwd_args *args, void *stream);
 
 /* Bytes of device workspace mm_attn_decode needs for these sizes (0 if invalid).
  * num_splits as in mm_decode_args (0 = automatic). */
@@ -184,6 +217,7 @@ const char *mm_status_str(int32_t status);
 /* sizeof of the argument structs, for bindings to check their mirrored layout. */
 size_t mm_fwd_args_size(void);
 size_t mm_decode_args_size(void);
+size_t mm_bwd_args_size(void);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t mm_version(void);

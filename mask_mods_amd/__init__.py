@@ -17,7 +17,8 @@ import math
 import os
 
 __all__ = [
-    "attn_fwd", "attn_decode", "decode_workspace_size", "decode_auto_splits", "block_mask_create",
+    "attn_fwd", "attn_bwd", "bwd_workspace_size", "attn_decode", "decode_workspace_size",
+    "decode_auto_splits", "block_mask_create",
     "MaskModsError", "library_path", "load_library",
     "SCORE_NONE", "SCORE_ALIBI", "MASK_CAUSAL", "MASK_WINDOW", "MASK_ROWDROP",
     "ROWDROP_5PCT", "BLOCK_Q", "BLOCK_KV", "BLOCK_EMPTY", "BLOCK_PARTIAL", "BLOCK_FULL",
@@ -79,6 +80,26 @@ class FwdArgs(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("Skv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("q_strides", ctypes.c_int64 * 3), ("k_strides", ctypes.c_int64 * 3),
+        ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3),
+        ("do_strides", ctypes.c_int64 * 3), ("dq_strides", ctypes.c_int64 * 3),
+        ("dk_strides", ctypes.c_int64 * 3), ("dv_strides", ctypes.c_int64 * 3),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("mods", _Mods),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class DecodeArgs(ctypes.Structure):
     _fields_ = [
         ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
@@ -123,6 +144,11 @@ def load_library():
     lib.mm_block_mask_create.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.mm_block_mask_create.restype = ctypes.c_int32
+    lib.mm_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+    lib.mm_attn_bwd.restype = ctypes.c_int32
+    lib.mm_attn_bwd_workspace_size.argtypes = [ctypes.c_int32] * 3
+    lib.mm_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mm_bwd_args_size.restype = ctypes.c_size_t
     lib.mm_status_str.argtypes = [ctypes.c_int32]
     lib.mm_status_str.restype = ctypes.c_char_p
     lib.mm_fwd_args_size.restype = ctypes.c_size_t
@@ -132,6 +158,8 @@ def load_library():
         raise RuntimeError("mm_fwd_args layout mismatch between library and binding")
     if lib.mm_decode_args_size() != ctypes.sizeof(DecodeArgs):
         raise RuntimeError("mm_decode_args layout mismatch between library and binding")
+    if lib.mm_bwd_args_size() != ctypes.sizeof(BwdArgs):
+        raise RuntimeError("mm_bwd_args layout mismatch between library and binding")
     _lib = lib
     return lib
 
@@ -278,6 +306,96 @@ def block_mask_create(Sq, Skv, *, causal=False, window=None, device=None, out=No
     if st != 0:
         raise MaskModsError(st, "mm_block_mask_create")
     return out
+
+
+def _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, Sq, Skv, B):
+    """Fill an mm_mods struct (shared by the forward and backward calls)."""
+    torch = _torch()
+    m = _Mods()
+    if isinstance(score_mod, str):
+        score_mod = {"none": SCORE_NONE, "alibi": SCORE_ALIBI}[score_mod]
+    flags = int(mask_flags)
+    if window is not None:
+        flags |= MASK_WINDOW
+    seed, thr = 0, 0
+    if rowdrop is not None:
+        flags |= MASK_ROWDROP
+        seed, thr = rowdrop
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (Hq,) \
+                or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be contiguous fp32 [Hq]")
+    bm_strides = (0, 0, 0)
+    if block_mask is not None:
+        nqb, nkb = -(-Sq // BLOCK_Q), -(-Skv // BLOCK_KV)
+        if block_mask.dtype != torch.uint8 or block_mask.dim() != 4:
+            raise ValueError("block_mask must be a 4-D uint8 tensor")
+        bb, bh, bq, bk = block_mask.shape
+        if bb not in (1, B) or bh not in (1, Hq) or bq < nqb or bk < nkb:
+            raise ValueError(f"block_mask shape {tuple(block_mask.shape)} does not cover "
+                             f"[{B}|1, {Hq}|1, {nqb}, {nkb}]")
+        if bk > 1 and block_mask.stride(3) != 1:
+            raise ValueError("block_mask's last dimension must be contiguous")
+        bm_strides = tuple(0 if n == 1 else st for n, st in zip(block_mask.shape[:3], block_mask.stride()[:3]))
+    m.score_mod = int(score_mod)
+    m.mask_flags = flags
+    m.window = int(window) if window is not None else 0
+    m.rowdrop_seed = seed & 0xFFFFFFFF
+    m.rowdrop_threshold = thr & 0xFFFFFFFF
+    m.alibi_slopes = alibi_slopes.data_ptr() if alibi_slopes is not None else None
+    m.block_mask = block_mask.data_ptr() if block_mask is not None and block_mask.numel() else None
+    m.block_mask_strides = _I64x3(*bm_strides)
+    return m
+
+
+def bwd_workspace_size(B, Hq, Sq) -> int:
+    return int(load_library().mm_attn_bwd_workspace_size(B, Hq, Sq))
+
+
+def attn_bwd(q, k, v, out, lse, dout, scale=None, *, causal=False, score_mod=SCORE_NONE,
+             alibi_slopes=None, mask_flags=0, window=None, rowdrop=None, block_mask=None,
+             workspace=None, dq=None, dk=None, dv=None):
+    """Backward of attn_fwd: gradients (dq, dk, dv) of sum(dout * out).
+
+    q, k, v, out, lse: the forward's inputs and outputs (lse is required); dout like out.
+    The mods must be the forward's. bf16 or f16, D in {64, 128}.
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = _check_dev(q, k, v, out, lse, dout, alibi_slopes, block_mask, workspace, dq, dk, dv)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shapes disagree")
+    if any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise ValueError("q/k/v/out/dout dtypes disagree")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be contiguous fp32 [B,Hq,Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_size(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(need // 4 + 4, dtype=torch.float32, device=dev)
+    a = BwdArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.out, a.dout, a.lse = out.data_ptr(), dout.data_ptr(), lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.dtype = _dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", out), ("do", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        setattr(a, name + "_strides", _I64x3(*t.stride()[:3]))
+    a.scale = float(scale)
+    a.causal = 1 if causal else 0
+    a.mods = _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, Sq, Skv, B)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mm_attn_bwd(ctypes.byref(a), _stream_ptr(dev))
+    if st != 0:
+        raise MaskModsError(st, "mm_attn_bwd")
+    return dq, dk, dv
 
 
 def decode_workspace_size(B, Hq, kv_len, D, num_splits=0) -> int:

@@ -38,6 +38,11 @@ SOURCES = [
     "fwd_f32.hip",
     "decode.hip",
     "block_mask.hip",
+    "bwd.hip",
+    "bwd_bf16_d128.hip",
+    "bwd_bf16_d64.hip",
+    "bwd_f16_d128.hip",
+    "bwd_f16_d64.hip",
 ]
 
 

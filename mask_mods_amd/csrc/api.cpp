@@ -51,6 +51,7 @@ int32_t mm_version(void) { return 200; }
 
 size_t mm_fwd_args_size(void) { return sizeof(mm_fwd_args); }
 size_t mm_decode_args_size(void) { return sizeof(mm_decode_args); }
+size_t mm_bwd_args_size(void) { return sizeof(mm_bwd_args); }
 
 const char *mm_status_str(int32_t st) {
     switch (st) {
@@ -176,6 +177,81 @@ mm_status mm_block_mask_create(uint32_t mask_flags, int32_t window, int32_t Sq, 
     if (ld < nkb) return MM_ERR_STRIDE;
     const hipError_t e = launch_block_mask(out, ld, Sq, Skv, (mask_flags & MM_MASK_CAUSAL) != 0,
                                            (mask_flags & MM_MASK_WINDOW) ? window : -1, (hipStream_t)stream);
+    return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
+}
+
+size_t mm_attn_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Sq) {
+    if (B < 0 || Hq <= 0 || Sq < 0) return 0;
+    const int64_t pad = ((int64_t)Sq + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad;
+    return (size_t)(2 * (int64_t)B * Hq * pad * (int64_t)sizeof(float));
+}
+
+mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
+    if (!a) return MM_ERR_NULL;
+    if (a->dtype != MM_F16 && a->dtype != MM_BF16) return MM_ERR_DTYPE;
+    if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0) return MM_ERR_SHAPE;
+    if (a->Hq % a->Hkv != 0) return MM_ERR_SHAPE;
+    if (a->D != 64 && a->D != 128) return MM_ERR_UNSUPPORTED;
+    const bool rows = (int64_t)a->B * a->Hq * a->Sq != 0, keys = (int64_t)a->B * a->Hkv * a->Skv != 0;
+    if (rows && (!a->q || !a->out || !a->dout || !a->lse || !a->dq)) return MM_ERR_NULL;
+    if (keys && (!a->k || !a->v || !a->dk || !a->dv)) return MM_ERR_NULL;
+    if (a->mods.score_mod != MM_SCORE_NONE && a->mods.score_mod != MM_SCORE_ALIBI) return MM_ERR_UNSUPPORTED;
+    if (a->mods.mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW | MM_MASK_ROWDROP))
+        return MM_ERR_UNSUPPORTED;
+    if ((a->mods.mask_flags & MM_MASK_WINDOW) && a->mods.window < 0) return MM_ERR_SHAPE;
+    if (a->mods.block_mask && bad_strides(a->mods.block_mask_strides, 3)) return MM_ERR_STRIDE;
+    if (!isfinite(a->scale)) return MM_ERR_SHAPE;
+    const int64_t *st[8] = {a->q_strides, a->k_strides, a->v_strides, a->o_strides,
+                            a->do_strides, a->dq_strides, a->dk_strides, a->dv_strides};
+    const void *ptr[8] = {a->q, a->k, a->v, a->out, a->dout, a->dq, a->dk, a->dv};
+    for (int t = 0; t < 8; ++t) {
+        if (bad_strides(st[t], 3) || strides_not_mult(st[t], 3, 8)) return MM_ERR_STRIDE;
+        if (misaligned16(ptr[t])) return MM_ERR_STRIDE;
+    }
+    // 32-bit byte offsets inside a copied tile: 64 K/V rows, 32 Q/dO rows
+    if ((64 * a->k_strides[2] + a->D) * 2 >= ((int64_t)1 << 31) ||
+        (64 * a->v_strides[2] + a->D) * 2 >= ((int64_t)1 << 31) ||
+        (32 * a->q_strides[2] + a->D) * 2 >= ((int64_t)1 << 31) ||
+        (32 * a->do_strides[2] + a->D) * 2 >= ((int64_t)1 << 31))
+        return MM_ERR_STRIDE;
+    if (!rows && !keys) return MM_OK;
+    const size_t need = mm_attn_bwd_workspace_size(a->B, a->Hq, a->Sq);
+    if (rows && (!a->workspace || a->workspace_bytes < need)) return MM_ERR_WORKSPACE;
+    if (((uintptr_t)a->workspace & 15u) != 0) return MM_ERR_WORKSPACE;
+    if ((int64_t)((a->Sq + kFwdBM - 1) / kFwdBM) * a->Hq * a->B > 0x7fffffff ||
+        (int64_t)((a->Skv + kFwdBM - 1) / kFwdBM) * a->Hkv * a->B > 0x7fffffff)
+        return MM_ERR_SHAPE;
+
+    BwdParams p = {};
+    p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = a->lse;
+    p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+    p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Sq = a->Sq; p.Skv = a->Skv; p.group = a->Hq / a->Hkv;
+    p.sq_pad = (a->Sq + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad;
+    p.ws_lse2 = (float *)a->workspace;
+    p.ws_dd = p.ws_lse2 + (int64_t)a->B * a->Hq * p.sq_pad;
+    p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_ss = a->q_strides[2];
+    p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_ss = a->k_strides[2];
+    p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_ss = a->v_strides[2];
+    p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_ss = a->o_strides[2];
+    p.do_sb = a->do_strides[0]; p.do_sh = a->do_strides[1]; p.do_ss = a->do_strides[2];
+    p.dq_sb = a->dq_strides[0]; p.dq_sh = a->dq_strides[1]; p.dq_ss = a->dq_strides[2];
+    p.dk_sb = a->dk_strides[0]; p.dk_sh = a->dk_strides[1]; p.dk_ss = a->dk_strides[2];
+    p.dv_sb = a->dv_strides[0]; p.dv_sh = a->dv_strides[1]; p.dv_ss = a->dv_strides[2];
+    p.scale = a->scale;
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    p.slopes = a->mods.alibi_slopes;
+    p.window = a->mods.window;
+    p.bm = a->mods.block_mask;
+    p.bm_sb = a->mods.block_mask_strides[0];
+    p.bm_sh = a->mods.block_mask_strides[1];
+    p.bm_sq = a->mods.block_mask_strides[2];
+    int mask = 0;
+    if (a->causal || (a->mods.mask_flags & MM_MASK_CAUSAL)) mask |= MASK_CAUSAL;
+    if (a->mods.mask_flags & MM_MASK_WINDOW) mask |= MASK_WINDOW;
+    if (a->mods.block_mask) mask |= MASK_BLOCK;
+    // the row-drop mod needs nothing here: dropped rows have LSE = -inf
+    const hipError_t e = launch_bwd(p, a->dtype, a->D, a->mods.score_mod == MM_SCORE_ALIBI, mask,
+                                    (hipStream_t)stream);
     return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
 }
 

@@ -1,0 +1,560 @@
+// bwd.h -- attention backward for gfx950 (bf16 / f16): dQ, dK, dV with the flex mods.
+//
+// For kept pairs, with P = exp(s - LSE) recomputed from the forward's LSE,
+//   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . V_j,   dS_ij = P_ij (dP_ij - D_i),
+//   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i,   D_i = dO_i . O_i.
+// Masked pairs, and rows with no kept key (LSE = -inf, which covers the row-drop mod),
+// contribute nothing. Three launches, no atomics:
+//   bwd_pre_kernel    D_i and LSE_i in base 2 (+inf for dead rows, so P = 2^(t - lse2) = 0)
+//   bwd_dq_kernel     shaped like the forward: a lane owns one query row; per 64-key tile
+//                     S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q^T / dO^T
+//                     held in VGPRs), then dQ^T += K^T dS^T (K^T by transpose reads, dS^T
+//                     from registers in the accumulator's key order)
+//   bwd_dkdv_kernel   a lane owns one key: per 32-row tile of Q and dO staged in LDS,
+//                     S = Q K^T and dP = dO V^T (B = K^T / V^T held in VGPRs), then
+//                     dV += P^T dO and dK += dS^T Q with dO^T / Q^T by transpose reads and
+//                     P^T / dS^T from registers; the loop runs over every query head of
+//                     the kv head's GQA group, so dK and dV are complete in one workgroup.
+// The tiles use the forward's swizzled layout and DMA copies (fwd_mfma.h, fwd_common.h).
+#pragma once
+
+#include "fwd_mfma.h"
+
+namespace mm {
+
+// ---- D_i = dO_i . O_i and lse2_i = LSE_i * log2(e) (+inf when LSE_i = -inf) ----
+template <typename TT, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+    constexpr int LPR = D / 8;  // lanes per row, 8 elements each
+    const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
+    const int64_t rid = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+    const int c = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (rid < nrows) {
+        const int i = (int)(rid % p.Sq);
+        const int h = (int)((rid / p.Sq) % p.Hq);
+        const int b = (int)(rid / ((int64_t)p.Sq * p.Hq));
+        const uint16_t *orow = (const uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_ss;
+        const uint16_t *drow = (const uint16_t *)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)i * p.do_ss;
+        const f32x8 ov = widen8(*(const u32x4 *)(orow + 8 * c), TT{});
+        const f32x8 dv = widen8(*(const u32x4 *)(drow + 8 * c), TT{});
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(ov[e], dv[e], acc);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (rid < nrows && c == 0) {
+        const int64_t w = (rid / p.Sq) * p.sq_pad + rid % p.Sq;
+        p.ws_dd[w] = acc;
+        const float l = p.lse[rid];
+        p.ws_lse2[w] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+}
+
+// ---- dQ: one workgroup = NW waves x 32 query rows of one (b, h) ----
+template <typename TT, int D, bool ALIBI, int MASK, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+    constexpr int BM = 32 * NW, BN = 64;
+    constexpr int KS = D / 16, DB = D / 32, NKB = BN / 32;
+    typedef Tile<D> TL;
+    constexpr int TILEB = BN * TL::ROWB;
+    constexpr int LOADS = TILEB / 1024 / NW;
+    constexpr int RPI = 1024 / TL::ROWB;
+    typedef typename TT::vec8 V8;
+    static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt_idx = L % p.n_tiles;
+    L /= p.n_tiles;
+    const int h = L % p.Hq;
+    const int b = L / p.Hq;
+    const int qt = (MASK & MASK_CAUSAL) ? (p.n_tiles - 1 - qt_idx) : qt_idx;
+    const int q0 = qt * BM;
+    const int hk = h / p.group;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int r0 = q0 + wave_s * 32;
+    const int row = r0 + l32;
+    const bool row_ok = row < p.Sq;
+
+    const uint16_t *kg = (const uint16_t *)p.k + b * p.k_sb + hk * p.k_sh;
+    const uint16_t *vg = (const uint16_t *)p.v + b * p.v_sb + hk * p.v_sh;
+
+    // Q^T and dO^T fragments (B operands): row `row`, dims 16*ks + 8*hi .. +7
+    V8 qf[KS], df[KS];
+    {
+        const int rr = row_ok ? row : 0;
+        const uint16_t *qr = (const uint16_t *)p.q + b * p.q_sb + h * p.q_sh + (int64_t)rr * p.q_ss + 8 * hi;
+        const uint16_t *dr = (const uint16_t *)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)rr * p.do_ss + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[ks] = as_vec<V8>(row_ok ? *(const u32x4 *)(qr + 16 * ks) : u32x4{0, 0, 0, 0});
+            df[ks] = as_vec<V8>(row_ok ? *(const u32x4 *)(dr + 16 * ks) : u32x4{0, 0, 0, 0});
+        }
+    }
+    const int64_t wid = ((int64_t)b * p.Hq + h) * p.sq_pad + (row_ok ? row : 0);
+    const float lse2 = row_ok ? p.ws_lse2[wid] : INFINITY;
+    const float ddr = row_ok ? p.ws_dd[wid] : 0.f;
+
+    const int row_max = min(q0 + BM, p.Sq) - 1;
+    int j_lo = 0, j_hi = p.Skv;
+    if ((MASK & MASK_CAUSAL) && !(MASK & MASK_BLOCK)) j_hi = min(j_hi, row_max + 1);
+    if ((MASK & MASK_WINDOW) && !(MASK & MASK_BLOCK)) {
+        j_lo = max(0, q0 - p.window);
+        if (!(MASK & MASK_CAUSAL)) j_hi = min(j_hi, row_max + p.window + 1);
+    }
+    const int kt_lo = j_lo / BN;
+    const int kt_hi = j_hi > j_lo ? (j_hi + BN - 1) / BN : kt_lo;
+
+    float slope2 = 0.f;
+    if (ALIBI) slope2 = (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e;
+    const float c2 = p.scale_log2;
+
+    int koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = TL::off(l32, 2 * ks + hi);
+    int voff[DB][2];  // transposed reads of a tile (K^T here), as the forward's V^T
+    {
+        const int G = lane >> 4, t = lane & 15;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int r = 8 * m2 + 4 * hi + (t >> 2);
+                const int d = 32 * db + 16 * (G & 1) + 4 * (t & 3);
+                voff[db][m2] = TL::off(r, d >> 3) + 2 * (d & 7);
+            }
+    }
+    uint32_t kgo[LOADS], vgo[LOADS];
+    int trow[LOADS], tchunk[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int r = (wave_s * LOADS + i) * RPI + lane / TL::CH;
+        const int c = (lane % TL::CH) ^ TL::swz(r);
+        trow[i] = r;
+        tchunk[i] = c;
+        kgo[i] = (uint32_t)(r * (int)p.k_ss + 8 * c) * 2u;
+        vgo[i] = (uint32_t)(r * (int)p.v_ss + 8 * c) * 2u;
+    }
+    auto load_tile = [&](int kt, unsigned char *kdst, unsigned char *vdst) {
+        const int k0 = kt * BN;
+        const uint32_t kl = lds_addr(kdst) + (uint32_t)(wave_s * LOADS) * 1024u;
+        const uint32_t vl = lds_addr(vdst) + (uint32_t)(wave_s * LOADS) * 1024u;
+        if (k0 + BN <= p.Skv) {
+            const char *kb = (const char *)(kg + (int64_t)k0 * p.k_ss);
+            const char *vb = (const char *)(vg + (int64_t)k0 * p.v_ss);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                dma16_sbase(kb, kgo[i], kl + i * 1024);
+                dma16_sbase(vb, vgo[i], vl + i * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int gr = min(k0 + trow[i], p.Skv - 1);
+                dma16_vaddr(kg + (int64_t)gr * p.k_ss + 8 * tchunk[i], kl + i * 1024);
+                dma16_vaddr(vg + (int64_t)gr * p.v_ss + 8 * tchunk[i], vl + i * 1024);
+            }
+        }
+    };
+
+    f32x16 dqacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
+
+    auto tile = [&](int kt, int blk, const unsigned char *Kt, const unsigned char *Vt, int next,
+                    unsigned char *Kn, unsigned char *Vn) {
+        if (next >= 0) load_tile(next, Kn, Vn);
+        const int k0 = kt * BN;
+        const int r_last = r0 + 31;
+        const bool pred = blk == 1;
+        bool skip = kt >= kt_hi, need_mask = k0 + BN > p.Skv;
+        if ((MASK & MASK_CAUSAL) && pred) {
+            skip |= k0 > r_last;
+            need_mask |= k0 + BN - 1 > r0;
+        }
+        if ((MASK & MASK_WINDOW) && pred) {
+            skip |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
+            need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
+        }
+        if (skip) return;
+        // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T, then dS^T, then
+        // dQ^T += K^T dS^T over the block's two 16-key k-steps
+        const bool general = ALIBI || need_mask;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 ka = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[ks]);
+                const u32x4 va = *(const u32x4 *)(Vt + kb * 32 * TL::ROWB + koff[ks]);
+                sacc = mfma32x32x16(as_vec<V8>(ka), qf[ks], sacc);
+                dpacc = mfma32x32x16(as_vec<V8>(va), df[ks], dpacc);
+            }
+            // P = 2^(t - lse2) and dS = P (dP - D) as 16-bit pairs, keys in accumulator order
+            uint32_t dsp[8];
+            auto make_ds = [&](bool gen) {
+                const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    float x[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int e = 2 * e2 + u;
+                        const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
+                        float pv;
+                        if (gen) {
+                            const float t = ALIBI ? fmaf(sacc[e], c2, fmaf(slope2, (float)jo, base)) : sacc[e] * c2;
+                            const int j = k0 + 4 * hi + jo;
+                            bool keep = j < p.Skv;
+                            if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
+                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                            pv = keep ? fast_exp2(t - lse2) : 0.f;
+                        } else {
+                            pv = fast_exp2(fmaf(sacc[e], c2, -lse2));
+                        }
+                        x[u] = pv * (dpacc[e] - ddr);
+                    }
+                    dsp[e2] = pack2(x[0], x[1], TT{});
+                }
+            };
+            if (general) make_ds(true);
+            else make_ds(false);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int ks = 2 * kb + half, o4 = 4 * half;
+                const V8 pf = as_vec<V8>(u32x4{dsp[o4], dsp[o4 + 1], dsp[o4 + 2], dsp[o4 + 3]});
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MM_LDS s16x4 *)(Kt + ks * 16 * TL::ROWB + voff[db][0]));
+                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MM_LDS s16x4 *)(Kt + ks * 16 * TL::ROWB + voff[db][1]));
+                    const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi4);
+                    dqacc[db] = mfma32x32x16(as_vec<V8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pf, dqacc[db]);
+                }
+            }
+        }
+    };
+
+    if (MASK & MASK_BLOCK) {
+        BlockWalk walk(p.bm + b * p.bm_sb + h * p.bm_sh + (int64_t)qt * p.bm_sq, kt_hi);
+        const int nkb = kt_hi;
+        int cv, nv;
+        int cur = walk.next(0, lane, cv);
+        int nxt = cur < nkb ? walk.next(cur + 1, lane, nv) : nkb;
+        if (cur < nkb) load_tile(cur, kv0, kv0 + TILEB);
+        kv_barrier<0>();
+        while (cur < nkb) {
+            tile(cur, cv, kv0, kv0 + TILEB, nxt < nkb ? nxt : -1, kv1, kv1 + TILEB);
+            kv_barrier<0>();
+            cur = nxt;
+            cv = nv;
+            if (cur >= nkb) break;
+            nxt = walk.next(cur + 1, lane, nv);
+            tile(cur, cv, kv1, kv1 + TILEB, nxt < nkb ? nxt : -1, kv0, kv0 + TILEB);
+            kv_barrier<0>();
+            cur = nxt;
+            cv = nv;
+            if (cur < nkb) nxt = walk.next(cur + 1, lane, nv);
+        }
+    } else {
+        if (kt_lo < kt_hi) load_tile(kt_lo, kv0, kv0 + TILEB);
+        kv_barrier<0>();
+        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+            tile(kt, 1, kv0, kv0 + TILEB, kt + 1 < kt_hi ? kt + 1 : -1, kv1, kv1 + TILEB);
+            kv_barrier<0>();
+            if (kt + 1 < kt_hi) {
+                tile(kt + 1, 1, kv1, kv1 + TILEB, kt + 2 < kt_hi ? kt + 2 : -1, kv0, kv0 + TILEB);
+                kv_barrier<0>();
+            }
+        }
+    }
+
+    if (row_ok) {
+        uint16_t *og = (uint16_t *)p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)row * p.dq_ss;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = {dqacc[db][4 * g4 + 0] * p.scale, dqacc[db][4 * g4 + 1] * p.scale,
+                                 dqacc[db][4 * g4 + 2] * p.scale, dqacc[db][4 * g4 + 3] * p.scale};
+                *(typename TT::vec4 *)(og + 32 * db + 8 * g4 + 4 * hi) = cvt4(x, TT{});
+            }
+    }
+}
+
+// ---- dK, dV: one workgroup = NW waves x 32 keys of one (b, kv head) ----
+// (one wave per SIMD: K^T, V^T and the dK, dV accumulators of a wave's 32 keys take
+// most of a 512-register budget, the dK/dV accumulators living in AGPRs)
+template <typename TT, int D, bool ALIBI, int MASK, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+    constexpr int BQ = 32;          // query rows per tile
+    constexpr int BNK = 32 * NW;    // keys per workgroup
+    constexpr int KS = D / 16, DB = D / 32;
+    typedef Tile<D> TL;
+    constexpr int TILEB = BQ * TL::ROWB;       // bytes of one Q (or dO) tile
+    constexpr int LOADS = TILEB / 1024 / NW;   // copies per wave per tensor per tile
+    constexpr int RPI = 1024 / TL::ROWB;
+    typedef typename TT::vec8 V8;
+    static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char qd0[2 * TILEB];  // Q tile, then dO tile
+    __shared__ __attribute__((aligned(1024))) unsigned char qd1[2 * TILEB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = L % p.n_tiles;
+    L /= p.n_tiles;
+    const int hk = L % p.Hkv;
+    const int b = L / p.Hkv;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int kw0 = kt * BNK + wave_s * 32;  // this wave's first key
+    const int key = kw0 + l32;               // the key this lane owns
+    const bool key_ok = key < p.Skv;
+
+    // K^T and V^T fragments (B operands): key `key`, dims 16*ks + 8*hi .. +7
+    V8 kf[KS], vf[KS];
+    {
+        const int kk = key_ok ? key : 0;
+        const uint16_t *kr = (const uint16_t *)p.k + b * p.k_sb + hk * p.k_sh + (int64_t)kk * p.k_ss + 8 * hi;
+        const uint16_t *vr = (const uint16_t *)p.v + b * p.v_sb + hk * p.v_sh + (int64_t)kk * p.v_ss + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kf[ks] = as_vec<V8>(key_ok ? *(const u32x4 *)(kr + 16 * ks) : u32x4{0, 0, 0, 0});
+            vf[ks] = as_vec<V8>(key_ok ? *(const u32x4 *)(vr + 16 * ks) : u32x4{0, 0, 0, 0});
+        }
+    }
+
+    // query rows that can see this workgroup's keys
+    const int kmin = kt * BNK, kmax = min(kt * BNK + BNK, p.Skv) - 1;
+    int i_lo = 0, i_hi = p.Sq;
+    if ((MASK & MASK_CAUSAL) && !(MASK & MASK_BLOCK)) i_lo = kmin;
+    if ((MASK & MASK_WINDOW) && !(MASK & MASK_BLOCK)) {
+        i_hi = min(i_hi, kmax + p.window + 1);
+        if (!(MASK & MASK_CAUSAL)) i_lo = max(0, kmin - p.window);
+    }
+    const int qt_lo = i_lo / BQ;
+    const int qt_hi = i_hi > i_lo ? (i_hi + BQ - 1) / BQ : qt_lo;
+    const int nq = qt_hi - qt_lo;
+    const int n_it = p.group * nq;  // (query head of the group, q tile) pairs
+
+    const float c2 = p.scale_log2;
+    int koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = TL::off(l32, 2 * ks + hi);
+    int voff[DB][2];
+    {
+        const int G = lane >> 4, t = lane & 15;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int r = 8 * m2 + 4 * hi + (t >> 2);
+                const int d = 32 * db + 16 * (G & 1) + 4 * (t & 3);
+                voff[db][m2] = TL::off(r, d >> 3) + 2 * (d & 7);
+            }
+    }
+    uint32_t qgo[LOADS], dgo[LOADS];
+    int trow[LOADS], tchunk[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int r = (wave_s * LOADS + i) * RPI + lane / TL::CH;
+        const int c = (lane % TL::CH) ^ TL::swz(r);
+        trow[i] = r;
+        tchunk[i] = c;
+        qgo[i] = (uint32_t)(r * (int)p.q_ss + 8 * c) * 2u;
+        dgo[i] = (uint32_t)(r * (int)p.do_ss + 8 * c) * 2u;
+    }
+    // copy the Q and dO rows of iteration n (query head h, tile qt)
+    auto load_tile = [&](int n, unsigned char *dst) {
+        const int h = hk * p.group + n / nq, i0 = (qt_lo + n % nq) * BQ;
+        const uint16_t *qg = (const uint16_t *)p.q + b * p.q_sb + h * p.q_sh;
+        const uint16_t *dg = (const uint16_t *)p.dout + b * p.do_sb + h * p.do_sh;
+        const uint32_t ql = lds_addr(dst) + (uint32_t)(wave_s * LOADS) * 1024u;
+        const uint32_t dl = ql + TILEB;
+        if (i0 + BQ <= p.Sq) {
+            const char *qb = (const char *)(qg + (int64_t)i0 * p.q_ss);
+            const char *db_ = (const char *)(dg + (int64_t)i0 * p.do_ss);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                dma16_sbase(qb, qgo[i], ql + i * 1024);
+                dma16_sbase(db_, dgo[i], dl + i * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int gr = min(i0 + trow[i], p.Sq - 1);
+                dma16_vaddr(qg + (int64_t)gr * p.q_ss + 8 * tchunk[i], ql + i * 1024);
+                dma16_vaddr(dg + (int64_t)gr * p.do_ss + 8 * tchunk[i], dl + i * 1024);
+            }
+        }
+    };
+
+    f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dkacc[db] = f32x16{};
+        dvacc[db] = f32x16{};
+    }
+
+    auto tile = [&](int n, const unsigned char *Qt, int next, unsigned char *Nn) {
+        if (next >= 0) load_tile(next, Nn);
+        const unsigned char *Dt = Qt + TILEB;
+        const int h = hk * p.group + n / nq, i0 = (qt_lo + n % nq) * BQ;
+        const int i_last = i0 + BQ - 1;
+        int blk = 1;
+        if ((MASK & MASK_BLOCK) && kw0 < p.Skv)
+            blk = p.bm[b * p.bm_sb + h * p.bm_sh + (int64_t)(i0 / kBlockQ) * p.bm_sq + kw0 / kBlockKV];
+        const bool pred = blk == 1;
+        bool skip = blk == 0 || kw0 >= p.Skv;
+        bool need_mask = kw0 + 31 >= p.Skv || i_last >= p.Sq;
+        if ((MASK & MASK_CAUSAL) && pred) {
+            skip |= i_last < kw0;
+            need_mask |= i0 < kw0 + 31;
+        }
+        if ((MASK & MASK_WINDOW) && pred) {
+            skip |= (kw0 - i_last > p.window) || (i0 - (kw0 + 31) > p.window);
+            need_mask |= max(i_last - kw0, kw0 + 31 - i0) > p.window;
+        }
+        if (skip) return;
+        // per-lane rows of the accumulator: i0 + 8*a + 4*hi + (0..3), a = 0..3 (16-byte
+        // aligned loads inside the (b, h) row block, which is padded to 32 rows; pad rows
+        // hold no data and are always masked)
+        const int64_t rbase = ((int64_t)b * p.Hq + h) * p.sq_pad + i0 + 4 * hi;
+        f32x4 l2[4], dd[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            l2[a] = *(const f32x4 *)(p.ws_lse2 + rbase + 8 * a);
+            dd[a] = *(const f32x4 *)(p.ws_dd + rbase + 8 * a);
+        }
+        // S = Q K^T and dP = dO V^T (a lane: one key, 16 rows)
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 qa = *(const u32x4 *)(Qt + koff[ks]);
+            const u32x4 da = *(const u32x4 *)(Dt + koff[ks]);
+            sacc = mfma32x32x16(as_vec<V8>(qa), kf[ks], sacc);
+            dpacc = mfma32x32x16(as_vec<V8>(da), vf[ks], dpacc);
+        }
+        float slope2 = 0.f;
+        if (ALIBI) slope2 = (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e;
+        uint32_t pp[8], dsp[8];
+        auto make = [&](bool general) {
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                float pv[2], ds[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int e = 2 * e2 + u;
+                    const int ro = 8 * (e >> 2) + (e & 3);  // row offset from i0 + 4*hi
+                    const float lse2 = l2[e >> 2][e & 3];
+                    float x;
+                    if (general) {
+                        const int i = i0 + 4 * hi + ro;
+                        const float t = ALIBI ? fmaf(sacc[e], c2, slope2 * (float)(key - i)) : sacc[e] * c2;
+                        bool keep = key_ok && i < p.Sq;
+                        if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
+                        if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
+                        x = keep ? fast_exp2(t - lse2) : 0.f;
+                        ds[u] = keep ? x * (dpacc[e] - dd[e >> 2][e & 3]) : 0.f;
+                    } else {
+                        x = fast_exp2(fmaf(sacc[e], c2, -lse2));
+                        ds[u] = x * (dpacc[e] - dd[e >> 2][e & 3]);
+                    }
+                    pv[u] = x;
+                }
+                pp[e2] = pack2(pv[0], pv[1], TT{});
+                dsp[e2] = pack2(ds[0], ds[1], TT{});
+            }
+        };
+        if (ALIBI || need_mask) make(true);
+        else make(false);
+        // dV += P^T dO and dK += dS^T Q over the tile's two 16-row k-steps
+#pragma unroll
+        for (int ks = 0; ks < BQ / 16; ++ks) {
+            const V8 pa = as_vec<V8>(u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]});
+            const V8 sa = as_vec<V8>(u32x4{dsp[4 * ks], dsp[4 * ks + 1], dsp[4 * ks + 2], dsp[4 * ks + 3]});
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MM_LDS s16x4 *)(Dt + ks * 16 * TL::ROWB + voff[db][0]));
+                const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MM_LDS s16x4 *)(Dt + ks * 16 * TL::ROWB + voff[db][1]));
+                const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MM_LDS s16x4 *)(Qt + ks * 16 * TL::ROWB + voff[db][0]));
+                const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MM_LDS s16x4 *)(Qt + ks * 16 * TL::ROWB + voff[db][1]));
+                const u32x2 d0 = __builtin_bit_cast(u32x2, dlo), d1 = __builtin_bit_cast(u32x2, dhi);
+                const u32x2 q0 = __builtin_bit_cast(u32x2, qlo), q1 = __builtin_bit_cast(u32x2, qhi);
+                dvacc[db] = mfma32x32x16(pa, as_vec<V8>(u32x4{d0[0], d0[1], d1[0], d1[1]}), dvacc[db]);
+                dkacc[db] = mfma32x32x16(sa, as_vec<V8>(u32x4{q0[0], q0[1], q1[0], q1[1]}), dkacc[db]);
+            }
+        }
+    };
+
+    if (n_it > 0) load_tile(0, qd0);
+    kv_barrier<0>();
+    for (int n = 0; n < n_it; n += 2) {
+        tile(n, qd0, n + 1 < n_it ? n + 1 : -1, qd1);
+        kv_barrier<0>();
+        if (n + 1 < n_it) {
+            tile(n + 1, qd1, n + 2 < n_it ? n + 2 : -1, qd0);
+            kv_barrier<0>();
+        }
+    }
+
+    // accumulator layout: lane holds dim 32*db + l32, keys kw0 + 8*(e/4) + 4*hi + e%4
+    uint16_t *dkg = (uint16_t *)p.dk + b * p.dk_sb + hk * p.dk_sh;
+    uint16_t *dvg = (uint16_t *)p.dv + b * p.dv_sb + hk * p.dv_sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = kw0 + 8 * (e >> 2) + 4 * hi + (e & 3);
+            if (j < p.Skv) {
+                dkg[(int64_t)j * p.dk_ss + 32 * db + l32] = narrow1(dkacc[db][e] * p.scale, TT{});
+                dvg[(int64_t)j * p.dv_ss + 32 * db + l32] = narrow1(dvacc[db][e], TT{});
+            }
+        }
+}
+
+template <typename TT, int D, bool A, int M>
+hipError_t launch_bwd_one(BwdParams p, hipStream_t s) {
+    constexpr int NW = 4;
+    const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
+    if (nrows > 0) {
+        const int rpb = 256 / (D / 8);
+        bwd_pre_kernel<TT, D><<<dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, s>>>(p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        BwdParams q = p;
+        q.n_tiles = (p.Sq + 32 * NW - 1) / (32 * NW);
+        bwd_dq_kernel<TT, D, A, M, NW><<<dim3((unsigned)(q.n_tiles * p.Hq * p.B)), dim3(64 * NW), 0, s>>>(q);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if ((int64_t)p.B * p.Hkv * p.Skv > 0) {
+        BwdParams k = p;
+        k.n_tiles = (p.Skv + 32 * NW - 1) / (32 * NW);
+        bwd_dkdv_kernel<TT, D, A, M, NW><<<dim3((unsigned)(k.n_tiles * p.Hkv * p.B)), dim3(64 * NW), 0, s>>>(k);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <typename TT, int D>
+hipError_t launch_bwd_t(const BwdParams &p, bool alibi, int mask, hipStream_t s) {
+#define MM_CASE(A, M) case (A) * 8 + (M): return launch_bwd_one<TT, D, (A) != 0, (M)>(p, s);
+    switch ((alibi ? 8 : 0) + (mask & 7)) {
+        MM_CASE(0, 0) MM_CASE(0, 1) MM_CASE(0, 2) MM_CASE(0, 3)
+        MM_CASE(0, 4) MM_CASE(0, 5) MM_CASE(0, 6) MM_CASE(0, 7)
+        MM_CASE(1, 0) MM_CASE(1, 1) MM_CASE(1, 2) MM_CASE(1, 3)
+        MM_CASE(1, 4) MM_CASE(1, 5) MM_CASE(1, 6) MM_CASE(1, 7)
+        default: return hipErrorInvalidValue;
+    }
+#undef MM_CASE
+}
+
+}  // namespace mm

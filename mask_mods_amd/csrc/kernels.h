@@ -33,6 +33,25 @@ struct FwdParams {
     float v_descale;       // fp8 inputs: V dequantisation factor (the Q/K ones are in scale_log2)
 };
 
+// Backward (dQ, dK, dV). Strides are in elements.
+struct BwdParams {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;      // forward LSE, natural log, [B, Hq, Sq] contiguous
+    void *dq, *dk, *dv;
+    float *ws_lse2;        // [B, Hq, sq_pad]: LSE * log2(e), +inf for rows with no kept key
+    float *ws_dd;          // [B, Hq, sq_pad]: rowsum(dO * O)
+    int B, Hq, Hkv, Sq, Skv, group;
+    int sq_pad;            // Sq rounded up to a multiple of 32 (rows of the workspace arrays)
+    int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
+    int64_t do_sb, do_sh, do_ss, dq_sb, dq_sh, dq_ss, dk_sb, dk_sh, dk_ss, dv_sb, dv_sh, dv_ss;
+    float scale, scale_log2;
+    const float *slopes;   // alibi slopes per query head (natural units) or nullptr
+    int window;
+    const uint8_t *bm;     // block mask or nullptr (as FwdParams)
+    int64_t bm_sb, bm_sh, bm_sq;
+    int n_tiles;           // q tiles (dQ kernel) or key tiles (dK/dV kernel) per head
+};
+
 // Decode split pass + merge. Strides are in elements.
 struct DecParams {
     const void *q, *k, *v;
@@ -63,6 +82,9 @@ hipError_t launch_fwd_fp8_d64(const FwdParams &p, bool alibi, int mask, hipStrea
 hipError_t launch_fwd_fp8_d128(const FwdParams &p, bool alibi, int mask, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams &p, int D, bool alibi, int mask, hipStream_t s);
 hipError_t launch_decode(const DecParams &p, int dtype, int D, hipStream_t s);
+// the three backward launches (pre-pass, dQ, dK/dV); dtype 1 = f16, 2 = bf16
+hipError_t launch_bwd(const BwdParams &p, int dtype, int D, bool alibi, int mask, hipStream_t s);
+constexpr int kBwdRowPad = 32;  // workspace rows per (b, h) are padded to this multiple
 // window < 0: no window predicate
 hipError_t launch_block_mask(uint8_t *out, int64_t ld, int Sq, int Skv, bool causal, int window,
                              hipStream_t s);

@@ -1,0 +1,146 @@
+"""GPU parity of the backward (mm_attn_bwd through the C ABI) against the oracle.
+
+The kernel backward consumes the kernel forward's O and LSE (as training does); the
+oracle computes its own forward in fp64. Every case prints its parameters first so a
+failing GPU step names itself.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import O_ATOL, O_RTOL, assert_parity, to_f64, to_torch
+from mask_mods_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+RD = (20240, int(0.05 * 2 ** 32))
+
+
+def _grads(B, Hq, Hkv, Sq, Skv, D, dtype, *, causal=False, window=None, alibi=False,
+           rowdrop=False, block_mask=None, seed=0, scale=None):
+    """Run forward + backward on the GPU; return device grads and the f64 inputs."""
+    import torch
+    import mask_mods_amd as mm
+    print(f"[bwd] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal} "
+          f"window={window} alibi={alibi} rowdrop={rowdrop} block={block_mask is not None} seed={seed}",
+          flush=True)
+    x = inputs.attention_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
+    g = inputs.rng(seed + 1000)
+    do_bits = inputs.f32_to_bits(g.standard_normal((B, Hq, Sq, D), dtype=np.float32), dtype)
+    q, k, v, do = (to_torch(b_, dtype) for b_ in (x["q"], x["k"], x["v"], do_bits))
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    kw = dict(causal=causal, window=window, score_mod=mm.SCORE_ALIBI if alibi else mm.SCORE_NONE,
+              rowdrop=RD if rowdrop else None,
+              block_mask=torch.from_numpy(block_mask).cuda() if block_mask is not None else None)
+    out, lse = mm.attn_fwd(q, k, v, scale, **kw)
+    dq, dk, dv = mm.attn_bwd(q, k, v, out, lse, do, scale, **kw)
+    torch.cuda.synchronize()
+    f64 = [inputs.bits_to_f64(b_, dtype) for b_ in (x["q"], x["k"], x["v"], do_bits)]
+    return (dq, dk, dv), f64, scale
+
+
+def _check(B, Hq, Hkv, Sq, Skv, D, dtype, **mods):
+    (dq, dk, dv), (qd, kd, vd, dod), scale = _grads(B, Hq, Hkv, Sq, Skv, D, dtype, **mods)
+    ref = oracle.attention_bwd(qd, kd, vd, dod, scale=scale, causal=mods.get("causal", False),
+                               window=mods.get("window"), alibi=mods.get("alibi", False),
+                               rowdrop=RD if mods.get("rowdrop") else None,
+                               block_mask=mods.get("block_mask"))
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        err = assert_parity(to_f64(got), want, O_ATOL, O_RTOL, name)
+        print(f"[bwd] {name} max|err| {err:.3e} max|ref| {np.abs(want).max():.3e}", flush=True)
+    return dq, dk, dv
+
+
+CASES = {
+    "none": dict(),
+    "causal": dict(causal=True),
+    "alibi": dict(alibi=True),
+    "alibi_causal": dict(alibi=True, causal=True),
+    "sliding_window": dict(window=64, causal=True),
+    "window_only": dict(window=40),
+    "rowdrop": dict(rowdrop=True, causal=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_matrix(dtype, D, case):
+    _check(1, 2, 2, 250, 250, D, dtype, seed=1, **CASES[case])
+
+
+def test_multi_tile_1024():
+    _check(1, 2, 2, 1024, 1024, 128, "bf16", seed=2, causal=True, alibi=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gqa(dtype):
+    _check(2, 8, 2, 300, 300, 128, dtype, seed=3, causal=True, alibi=True)
+    _check(1, 8, 1, 129, 257, 64, dtype, seed=4, window=33)
+
+
+@pytest.mark.parametrize("shape,mods", [
+    ((200, 700), dict(alibi=True)),
+    ((700, 200), dict(causal=True)),
+    ((129, 1000), dict(window=40)),
+    ((1, 300), dict()),
+    ((300, 1), dict(causal=True)),
+    ((600, 130), dict(causal=True, window=100)),  # rows >= 231 see no key
+])
+def test_cross_attention(shape, mods):
+    Sq, Skv = shape
+    _check(1, 4, 2, Sq, Skv, 128, "bf16", seed=5, **mods)
+
+
+@pytest.mark.parametrize("pred", ["none", "causal"])
+def test_block_mask(pred):
+    S = 384
+    bm = inputs.random_block_mask(6, (1, 4, -(-S // 128), -(-S // 64)))
+    _check(1, 4, 2, S, S, 128, "bf16", seed=6, block_mask=bm, **({"causal": True} if pred == "causal" else {}))
+
+
+def test_created_causal_classes_match_plain_causal_bitwise():
+    import torch
+    import mask_mods_amd as mm
+    S = 700
+    bm = mm.block_mask_create(S, S, causal=True)
+    ga, _, _ = _grads(1, 2, 2, S, S, 128, "bf16", seed=7, causal=True, block_mask=bm.cpu().numpy())
+    gb, _, _ = _grads(1, 2, 2, S, S, 128, "bf16", seed=7, causal=True)
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y)
+
+
+def test_fully_masked_rows_and_empty_keys():
+    dq, _, _ = _check(1, 2, 2, 600, 130, 64, "bf16", seed=8, causal=True, window=100)
+    assert np.all(to_f64(dq)[:, :, 231:] == 0)
+    import torch
+    import mask_mods_amd as mm
+    q = torch.randn(1, 2, 40, 128, device="cuda", dtype=torch.bfloat16)
+    k = torch.empty(1, 2, 0, 128, device="cuda", dtype=torch.bfloat16)
+    out, lse = mm.attn_fwd(q, k, k.clone(), 0.1)
+    dq, dk, dv = mm.attn_bwd(q, k, k.clone(), out, lse, torch.randn_like(q), 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and dk.numel() == 0
+
+
+def test_deterministic():
+    import torch
+    g1, _, _ = _grads(1, 4, 2, 512, 512, 128, "bf16", seed=9, causal=True)
+    g2, _, _ = _grads(1, 4, 2, 512, 512, 128, "bf16", seed=9, causal=True)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_config_2048_sampled_heads(causal):
+    """B2 H32 D128 S2048 on the GPU; the oracle recomputes two (b, h) heads in full."""
+    B, H, S, D = 2, 32, 2048, 128
+    (dq, dk, dv), (qd, kd, vd, dod), scale = _grads(B, H, H, S, S, D, "bf16", seed=10, causal=causal)
+    for b, h in ((0, 0), (1, 31)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_bwd(qd[sl], kd[sl], vd[sl], dod[sl], scale=scale, causal=causal)
+        for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            assert_parity(to_f64(got[sl]), want, O_ATOL, O_RTOL, f"{name}[{b},{h}]")
