@@ -203,6 +203,19 @@ def profile_one(args, torch, mm, inputs, dev):
         scale = float(np.float32(1.0 / math.sqrt(D)))
         fn = lambda: mm.attn_fwd(q8, k8, v8, scale, descale=(sq, sk, sv), out=out, lse=lse)
         unit_bytes = fp8_bytes(B, H, S, D)
+    elif args.only == "bwd":
+        B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        out, lse = mm.attn_fwd(q, k, v, scale)
+        g = np.random.default_rng(11)
+        dout = torch.from_numpy(g.standard_normal((B, H, S, D), dtype=np.float32)).to(dev).bfloat16()
+        ws = torch.empty(mm.bwd_workspace_size(B, H, S) // 4 + 4, dtype=torch.float32, device=dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        fn = lambda: mm.attn_bwd(q, k, v, out, lse, dout, scale, workspace=ws,
+                                 dq=grads[0], dk=grads[1], dv=grads[2])
+        unit_bytes = 8 * B * H * S * D * 2 + 2 * B * H * S * 4  # q k v o dO in, dq dk dv out, lse
     elif args.only == "fwd":
         B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
         x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
@@ -242,7 +255,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--only", choices=["fwd", "fp8", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fp8", "bwd", "decode", "copy"], default=None,
                     help="profiling aid: run just one kernel family (or a plain 1 GiB device copy "
                          "used to calibrate the HBM byte counters) and print its timing")
     ap.add_argument("--ingest", metavar="DIR", default=None,
@@ -412,6 +425,37 @@ def main():
         },
         "cases_s8192": cases,
     }
+    # backward (bf16, same shape): dq, dk, dv of sum(dO * O) from the forward's O and LSE
+    if not args.no_cases:
+        g = np.random.default_rng(11)
+        dout = torch.from_numpy(g.standard_normal((B, H, S, D), dtype=np.float32)).to(dev).bfloat16()
+        bws = torch.empty(mm.bwd_workspace_size(B, H, S) // 4 + 4, dtype=torch.float32, device=dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        bwd = {}
+        for name, kw in (("no_mod", {}), ("causal", dict(causal=True))):
+            o_b = torch.empty_like(q)
+            l_b = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+            mm.attn_fwd(q, k, v, scale, out=o_b, lse=l_b, **kw)
+            run = lambda: mm.attn_bwd(q, k, v, o_b, l_b, dout, scale, workspace=bws,
+                                      dq=grads[0], dk=grads[1], dv=grads[2], **kw)
+            for _ in range(3):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 10
+            e0.record(stream)
+            for _ in range(n):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / n * 1e-3
+            # five products of the forward's size (S and dP recomputed, dV, dK, dQ):
+            # 2.5 x the forward's flops (half for causal)
+            alg = 2.5 * fwd_flops(B, H, S, S, D) * (0.5 if kw else 1.0)
+            bwd[name] = {"us": round(t * 1e6, 1), "tflops_algorithmic": round(alg / t / 1e12, 1),
+                         "frac_bf16_peak": round(alg / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        res["bwd"] = {"workload": "bf16 B2 H32 D128 S8192, dq/dk/dv from the forward's O and LSE",
+                      "algorithmic": "2.5 x 4*B*H*S*S*D flop (five S-sized products; causal half)",
+                      **bwd}
     if "fp8_no_mod" in cases:
         c8 = cases["fp8_no_mod"]
         a8 = fwd_flops(B, H, S, S, D) / (c8["us"] * 1e-6) / 1e12

@@ -10,7 +10,7 @@
 //                     S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q^T / dO^T
 //                     held in VGPRs), then dQ^T += K^T dS^T (K^T by transpose reads, dS^T
 //                     from registers in the accumulator's key order)
-//   bwd_dkdv_kernel   a lane owns one key: per 32-row tile of Q and dO staged in LDS,
+//   bwd_dkdv_kernel   a lane owns one key: per 64-row tile of Q and dO staged in LDS,
 //                     S = Q K^T and dP = dO V^T (B = K^T / V^T held in VGPRs), then
 //                     dV += P^T dO and dK += dS^T Q with dO^T / Q^T by transpose reads and
 //                     P^T / dS^T from registers; the loop runs over every query head of
@@ -289,11 +289,13 @@ void bwd_dq_kernel(BwdParams p) {
 
 // ---- dK, dV: one workgroup = NW waves x 32 keys of one (b, kv head) ----
 // (one wave per SIMD: K^T, V^T and the dK, dV accumulators of a wave's 32 keys take
-// most of a 512-register budget, the dK/dV accumulators living in AGPRs)
+// most of a 512-register budget, the dK/dV accumulators living in AGPRs; 64-row query
+// tiles give four independent MFMA chains for S and dP)
 template <typename TT, int D, bool ALIBI, int MASK, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
-    constexpr int BQ = 32;          // query rows per tile
+    constexpr int BQ = 64;          // query rows per tile
+    constexpr int RB = BQ / 32;     // 32-row blocks per tile
     constexpr int BNK = 32 * NW;    // keys per workgroup
     constexpr int KS = D / 16, DB = D / 32;
     typedef Tile<D> TL;
@@ -302,9 +304,12 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int RPI = 1024 / TL::ROWB;
     typedef typename TT::vec8 V8;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
+    static_assert(kBwdRowPad % BQ == 0, "workspace row padding");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char qd0[2 * TILEB];  // Q tile, then dO tile
-    __shared__ __attribute__((aligned(1024))) unsigned char qd1[2 * TILEB];
+    // per stage: Q tile, dO tile, then the tile rows' lse2 and D (64 floats each)
+    constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;
+    __shared__ __attribute__((aligned(1024))) unsigned char qd0[STAGEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char qd1[STAGEB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -378,6 +383,13 @@ void bwd_dkdv_kernel(BwdParams p) {
         const uint16_t *dg = (const uint16_t *)p.dout + b * p.do_sb + h * p.do_sh;
         const uint32_t ql = lds_addr(dst) + (uint32_t)(wave_s * LOADS) * 1024u;
         const uint32_t dl = ql + TILEB;
+        if (wave_s == 0) {
+            // the rows' lse2 and D (the (b, h) row block is padded to whole tiles)
+            const int64_t w = ((int64_t)b * p.Hq + h) * p.sq_pad + i0 + lane;
+            const uint32_t sl = lds_addr(dst) + 2 * TILEB;
+            dma4_vaddr(p.ws_lse2 + w, sl);
+            dma4_vaddr(p.ws_dd + w, sl + BQ * 4);
+        }
         if (i0 + BQ <= p.Sq) {
             const char *qb = (const char *)(qg + (int64_t)i0 * p.q_ss);
             const char *db_ = (const char *)(dg + (int64_t)i0 * p.do_ss);
@@ -423,63 +435,73 @@ void bwd_dkdv_kernel(BwdParams p) {
             need_mask |= max(i_last - kw0, kw0 + 31 - i0) > p.window;
         }
         if (skip) return;
-        // per-lane rows of the accumulator: i0 + 8*a + 4*hi + (0..3), a = 0..3 (16-byte
-        // aligned loads inside the (b, h) row block, which is padded to 32 rows; pad rows
-        // hold no data and are always masked)
-        const int64_t rbase = ((int64_t)b * p.Hq + h) * p.sq_pad + i0 + 4 * hi;
-        f32x4 l2[4], dd[4];
+        // per-lane rows of block rb of the accumulator: i0 + 32*rb + 8*a + 4*hi + (0..3),
+        // their lse2 and D from the copy in LDS (pad rows hold no data and are masked)
+        const float *sl2 = (const float *)(Qt + 2 * TILEB), *sdd = sl2 + BQ;
+        f32x4 l2[RB][4], dd[RB][4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            l2[a] = *(const f32x4 *)(p.ws_lse2 + rbase + 8 * a);
-            dd[a] = *(const f32x4 *)(p.ws_dd + rbase + 8 * a);
-        }
-        // S = Q K^T and dP = dO V^T (a lane: one key, 16 rows)
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 qa = *(const u32x4 *)(Qt + koff[ks]);
-            const u32x4 da = *(const u32x4 *)(Dt + koff[ks]);
-            sacc = mfma32x32x16(as_vec<V8>(qa), kf[ks], sacc);
-            dpacc = mfma32x32x16(as_vec<V8>(da), vf[ks], dpacc);
+            for (int a = 0; a < 4; ++a) {
+                l2[rb][a] = *(const f32x4 *)(sl2 + 32 * rb + 8 * a + 4 * hi);
+                dd[rb][a] = *(const f32x4 *)(sdd + 32 * rb + 8 * a + 4 * hi);
+            }
+        // S = Q K^T and dP = dO V^T (a lane: one key, 16 rows per 32-row block)
+        f32x16 sacc[RB], dpacc[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            sacc[rb] = f32x16{};
+            dpacc[rb] = f32x16{};
         }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const u32x4 qa = *(const u32x4 *)(Qt + rb * 32 * TL::ROWB + koff[ks]);
+                const u32x4 da = *(const u32x4 *)(Dt + rb * 32 * TL::ROWB + koff[ks]);
+                sacc[rb] = mfma32x32x16(as_vec<V8>(qa), kf[ks], sacc[rb]);
+                dpacc[rb] = mfma32x32x16(as_vec<V8>(da), vf[ks], dpacc[rb]);
+            }
         float slope2 = 0.f;
         if (ALIBI) slope2 = (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e;
-        uint32_t pp[8], dsp[8];
+        uint32_t pp[RB][8], dsp[RB][8];
         auto make = [&](bool general) {
 #pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) {
-                float pv[2], ds[2];
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int e = 2 * e2 + u;
-                    const int ro = 8 * (e >> 2) + (e & 3);  // row offset from i0 + 4*hi
-                    const float lse2 = l2[e >> 2][e & 3];
-                    float x;
-                    if (general) {
-                        const int i = i0 + 4 * hi + ro;
-                        const float t = ALIBI ? fmaf(sacc[e], c2, slope2 * (float)(key - i)) : sacc[e] * c2;
-                        bool keep = key_ok && i < p.Sq;
-                        if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
-                        if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
-                        x = keep ? fast_exp2(t - lse2) : 0.f;
-                        ds[u] = keep ? x * (dpacc[e] - dd[e >> 2][e & 3]) : 0.f;
-                    } else {
-                        x = fast_exp2(fmaf(sacc[e], c2, -lse2));
-                        ds[u] = x * (dpacc[e] - dd[e >> 2][e & 3]);
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    float pv[2], ds[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int e = 2 * e2 + u;
+                        const float lse2 = l2[rb][e >> 2][e & 3];
+                        float x;
+                        if (general) {
+                            const int i = i0 + 32 * rb + 4 * hi + 8 * (e >> 2) + (e & 3);
+                            const float t = ALIBI ? fmaf(sacc[rb][e], c2, slope2 * (float)(key - i)) : sacc[rb][e] * c2;
+                            bool keep = key_ok && i < p.Sq;
+                            if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
+                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
+                            x = keep ? fast_exp2(t - lse2) : 0.f;
+                            ds[u] = keep ? x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]) : 0.f;
+                        } else {
+                            x = fast_exp2(fmaf(sacc[rb][e], c2, -lse2));
+                            ds[u] = x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]);
+                        }
+                        pv[u] = x;
                     }
-                    pv[u] = x;
+                    pp[rb][e2] = pack2(pv[0], pv[1], TT{});
+                    dsp[rb][e2] = pack2(ds[0], ds[1], TT{});
                 }
-                pp[e2] = pack2(pv[0], pv[1], TT{});
-                dsp[e2] = pack2(ds[0], ds[1], TT{});
-            }
         };
         if (ALIBI || need_mask) make(true);
         else make(false);
-        // dV += P^T dO and dK += dS^T Q over the tile's two 16-row k-steps
+        // dV += P^T dO and dK += dS^T Q over the tile's 16-row k-steps
 #pragma unroll
         for (int ks = 0; ks < BQ / 16; ++ks) {
-            const V8 pa = as_vec<V8>(u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]});
-            const V8 sa = as_vec<V8>(u32x4{dsp[4 * ks], dsp[4 * ks + 1], dsp[4 * ks + 2], dsp[4 * ks + 3]});
+            const int rb = ks >> 1, o4 = 4 * (ks & 1);
+            const V8 pa = as_vec<V8>(u32x4{pp[rb][o4], pp[rb][o4 + 1], pp[rb][o4 + 2], pp[rb][o4 + 3]});
+            const V8 sa = as_vec<V8>(u32x4{dsp[rb][o4], dsp[rb][o4 + 1], dsp[rb][o4 + 2], dsp[rb][o4 + 3]});
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MM_LDS s16x4 *)(Dt + ks * 16 * TL::ROWB + voff[db][0]));

@@ -32,6 +32,11 @@ __device__ __forceinline__ void dma16_vaddr(const void *gaddr, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  ::"v"(gaddr), "s"(lds) : "memory", "m0");
 }
+// 4 bytes per lane (64 lanes: 256 contiguous bytes), LDS destination M0 + 4*lane
+__device__ __forceinline__ void dma4_vaddr(const void *gaddr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 ::"v"(gaddr), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const MM_LDS void *)p;

@@ -41,7 +41,7 @@ struct BwdParams {
     float *ws_lse2;        // [B, Hq, sq_pad]: LSE * log2(e), +inf for rows with no kept key
     float *ws_dd;          // [B, Hq, sq_pad]: rowsum(dO * O)
     int B, Hq, Hkv, Sq, Skv, group;
-    int sq_pad;            // Sq rounded up to a multiple of 32 (rows of the workspace arrays)
+    int sq_pad;            // Sq rounded up to a multiple of kBwdRowPad (rows of the workspace arrays)
     int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
     int64_t do_sb, do_sh, do_ss, dq_sb, dq_sh, dq_ss, dk_sb, dk_sh, dk_ss, dv_sb, dv_sh, dv_ss;
     float scale, scale_log2;
@@ -84,7 +84,7 @@ hipError_t launch_fwd_f32(const FwdParams &p, int D, bool alibi, int mask, hipSt
 hipError_t launch_decode(const DecParams &p, int dtype, int D, hipStream_t s);
 // the three backward launches (pre-pass, dQ, dK/dV); dtype 1 = f16, 2 = bf16
 hipError_t launch_bwd(const BwdParams &p, int dtype, int D, bool alibi, int mask, hipStream_t s);
-constexpr int kBwdRowPad = 32;  // workspace rows per (b, h) are padded to this multiple
+constexpr int kBwdRowPad = 64;  // workspace rows per (b, h) are padded to this multiple
 // window < 0: no window predicate
 hipError_t launch_block_mask(uint8_t *out, int64_t ld, int Sq, int Skv, bool causal, int window,
                              hipStream_t s);
