@@ -425,6 +425,50 @@ def main():
         },
         "cases_s8192": cases,
     }
+    # decode variants: GQA (Hq 32 / Hkv 8: K/V streamed once per kv head) and a paged
+    # cache (B 8, 64-key pages scattered over a pool by a seeded permutation)
+    if not args.no_cases:
+        dcases = {}
+        def time_dec(fn, n=20):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n * 1e-3
+        Hkv_g = 8
+        xg = inputs.decode_inputs(3, 1, Hd, Hkv_g, [L], Dd, "f16")
+        gq, gk, gv, gm = (dev_tensor(xg[n], "f16") for n in ("q", "k", "v", "mask"))
+        gws = torch.empty(mm.decode_workspace_size(1, Hd, L, Dd, Hkv=Hkv_g) // 4 + 4, dtype=torch.float32, device=dev)
+        t = time_dec(lambda: mm.attn_decode(gq, gk, gv, L, dscale, mask=gm, workspace=gws))
+        gbytes = 1 * Hkv_g * L * Dd * 2 * 2 + 1 * Hd * L * 2 + 2 * 1 * Hd * Dd * 2 + 1 * Hd * 4
+        dcases["gqa_b1_h32_kv8_l32768"] = {"us": round(t * 1e6, 2), "GBs": round(gbytes / t / 1e9, 1),
+                                           "bytes": gbytes}
+        Bp, page = 8, 64
+        pages = L // page
+        gp = np.random.default_rng(5)
+        perm = torch.from_numpy(gp.permutation(Bp * pages).reshape(Bp, pages).astype(np.int32)).to(dev)
+        pk = torch.randn(Bp * pages, Hd, page, Dd, device=dev).half()
+        pv = torch.randn_like(pk)
+        pq = torch.randn(Bp, Hd, 1, Dd, device=dev).half()
+        pws = torch.empty(mm.decode_workspace_size(Bp, Hd, L, Dd) // 4 + 4, dtype=torch.float32, device=dev)
+        t = time_dec(lambda: mm.attn_decode(pq, pk, pv, L, dscale, workspace=pws, block_table=perm))
+        pbytes = Bp * Hd * L * Dd * 2 * 2 + 2 * Bp * Hd * Dd * 2 + Bp * Hd * 4 + Bp * pages * 4
+        dcases["paged_b8_h32_l32768_page64"] = {"us": round(t * 1e6, 2), "GBs": round(pbytes / t / 1e9, 1),
+                                                "bytes": pbytes}
+        ck = torch.randn(Bp, Hd, L, Dd, device=dev).half()
+        cv = torch.randn_like(ck)
+        del pk, pv
+        t = time_dec(lambda: mm.attn_decode(pq, ck, cv, L, dscale, workspace=pws))
+        cbytes = Bp * Hd * L * Dd * 2 * 2 + 2 * Bp * Hd * Dd * 2 + Bp * Hd * 4
+        dcases["contiguous_b8_h32_l32768"] = {"us": round(t * 1e6, 2), "GBs": round(cbytes / t / 1e9, 1),
+                                              "bytes": cbytes}
+        del ck, cv
+        res["decode_cases"] = dcases
+
     # backward (bf16, same shape): dq, dk, dv of sum(dO * O) from the forward's O and LSE
     if not args.no_cases:
         g = np.random.default_rng(11)

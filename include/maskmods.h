@@ -149,6 +149,16 @@ typedef struct mm_decode_args {
     void *workspace;         /* device scratch, >= mm_attn_decode_workspace_size()    */
     size_t workspace_bytes;
     int32_t num_splits;      /* 0 = automatic; else the KV split count to use         */
+    /* Paged KV cache (the dynamic batch of the IREE issue with a page table): if
+     * block_table is non-NULL, k_cache / v_cache are page pools [pages, Hkv, page_size,
+     * D] with kv_strides = (page, head, row) strides, and position j of sequence b is row
+     * j % page_size of page block_table[b * block_table_stride + j / page_size]. Entries
+     * covering positions below the sequence's length must be valid page ids; no other
+     * entry is read. page_size: a power of two. Scap is the logical capacity; with B > 1
+ * the table's row stride must cover ceil(Scap / page_size) entries. */
+    const int32_t *block_table;   /* device int32, or NULL for contiguous caches      */
+    int64_t block_table_stride;   /* elements between sequences' rows of the table    */
+    int32_t page_size;
 } mm_decode_args;
 
 typedef struct mm_bwd_args {
@@ -189,14 +199,16 @@ mm_status mm_attn_bwd(const mm_bwd_args *args, void *stream);
 
 /* Bytes of device workspace mm_attn_decode needs for these sizes (0 if invalid).
  * num_splits as in mm_decode_args (0 = automatic). */
-size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t kv_len, int32_t D,
+size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t D,
                                      int32_t num_splits);
 
-/* Decode attention (two launches on `stream`: split pass, then merge). */
+/* Decode attention (two launches on `stream`: split pass, then merge). With GQA
+ * (Hq > Hkv) one workgroup of the split pass serves up to 8 query heads of a kv head,
+ * so K/V are streamed once per kv head. */
 mm_status mm_attn_decode(const mm_decode_args *args, void *stream);
 
 /* Split count mm_attn_decode uses when num_splits == 0. */
-int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t kv_len);
+int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len);
 
 /* Block-mask classes of the built-in mask_mods, the analogue of building a BlockMask
  * from a mask_mod: out[qb*ld + kb] (device bytes, qb < ceil(Sq/MM_BLOCK_Q),

@@ -113,6 +113,9 @@ class DecodeArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("num_splits", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+        ("block_table_stride", ctypes.c_int64),
+        ("page_size", ctypes.c_int32),
     ]
 
 
@@ -137,9 +140,9 @@ def load_library():
     lib.mm_attn_fwd.restype = ctypes.c_int32
     lib.mm_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
     lib.mm_attn_decode.restype = ctypes.c_int32
-    lib.mm_attn_decode_workspace_size.argtypes = [ctypes.c_int32] * 5
+    lib.mm_attn_decode_workspace_size.argtypes = [ctypes.c_int32] * 6
     lib.mm_attn_decode_workspace_size.restype = ctypes.c_size_t
-    lib.mm_attn_decode_auto_splits.argtypes = [ctypes.c_int32] * 3
+    lib.mm_attn_decode_auto_splits.argtypes = [ctypes.c_int32] * 4
     lib.mm_attn_decode_auto_splits.restype = ctypes.c_int32
     lib.mm_block_mask_create.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
@@ -398,28 +401,43 @@ def attn_bwd(q, k, v, out, lse, dout, scale=None, *, causal=False, score_mod=SCO
     return dq, dk, dv
 
 
-def decode_workspace_size(B, Hq, kv_len, D, num_splits=0) -> int:
-    return int(load_library().mm_attn_decode_workspace_size(B, Hq, kv_len, D, num_splits))
+def decode_workspace_size(B, Hq, kv_len, D, num_splits=0, Hkv=None) -> int:
+    Hkv = Hq if Hkv is None else Hkv
+    return int(load_library().mm_attn_decode_workspace_size(B, Hq, Hkv, kv_len, D, num_splits))
 
 
-def decode_auto_splits(B, Hq, kv_len) -> int:
-    return int(load_library().mm_attn_decode_auto_splits(B, Hq, kv_len))
+def decode_auto_splits(B, Hq, kv_len, Hkv=None) -> int:
+    Hkv = Hq if Hkv is None else Hkv
+    return int(load_library().mm_attn_decode_auto_splits(B, Hq, Hkv, kv_len))
 
 
 def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
-                return_lse=True, num_splits=0, workspace=None, out=None, lse=None):
+                return_lse=True, num_splits=0, workspace=None, out=None, lse=None,
+                block_table=None):
     """Decode attention: q [B,Hq,1,D] against caches [B,Hkv,Scap,D] (f16/bf16).
 
     kv_len: number of cache positions in use (<= Scap). mask: optional f16
     additive mask [B,Hq,1,Scap] (last dim contiguous). seq_lens: optional int32
     device tensor [B] of per-sequence lengths (<= kv_len).
+    block_table: optional int32 device tensor [B, max_pages]; the caches are then page
+    pools [pages, Hkv, page_size, D] (page_size a power of two) and Scap is
+    max_pages * page_size.
     Returns (out [B,Hq,1,D], lse fp32 [B,Hq] or None).
     """
     torch = _torch()
     lib = load_library()
-    dev = _check_dev(q, k_cache, v_cache, mask, seq_lens, out, lse, workspace)
+    dev = _check_dev(q, k_cache, v_cache, mask, seq_lens, out, lse, workspace, block_table)
     B, Hq, one, D = q.shape
-    Bk, Hkv, Scap, Dk = k_cache.shape
+    if block_table is not None:
+        _, Hkv, page_size, Dk = k_cache.shape
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+                or (block_table.shape[1] > 1 and block_table.stride(1) != 1):
+            raise ValueError("block_table must be int32 [B, max_pages] with unit column stride")
+        Scap = block_table.shape[1] * page_size
+        Bk = B
+    else:
+        Bk, Hkv, Scap, Dk = k_cache.shape
+        page_size = 0
     if one != 1 or Bk != B or Dk != D or v_cache.shape != k_cache.shape:
         raise ValueError("decode shapes disagree")
     if k_cache.stride() != v_cache.stride():
@@ -435,7 +453,7 @@ def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
         out = torch.empty((B, Hq, 1, D), dtype=q.dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    need = lib.mm_attn_decode_workspace_size(B, Hq, int(kv_len), D, int(num_splits))
+    need = lib.mm_attn_decode_workspace_size(B, Hq, Hkv, int(kv_len), D, int(num_splits))
     if workspace is None:
         workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=dev)
     a = DecodeArgs()
@@ -453,6 +471,10 @@ def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.num_splits = int(num_splits)
+    if block_table is not None:
+        a.block_table = block_table.data_ptr()
+        a.block_table_stride = block_table.stride(0)
+        a.page_size = int(page_size)
     st = lib.mm_attn_decode(ctypes.byref(a), _stream_ptr(dev))
     if st != 0:
         raise MaskModsError(st, "mm_attn_decode")

@@ -31,10 +31,19 @@ bool strides_not_mult(const int64_t *s, int n, int m) {
     return false;
 }
 
-int decode_splits(int32_t B, int32_t Hq, int32_t kv_len, int32_t requested) {
+// query heads per split workgroup: the largest of 8, 4, 2, 1 dividing the GQA group
+int decode_heads_per_wg(int32_t Hq, int32_t Hkv) {
+    const int group = Hq / Hkv;
+    for (int g = 8; g > 1; g >>= 1)
+        if (group % g == 0) return g;
+    return 1;
+}
+
+// splits: enough (split, head group, batch) workgroups for about one resident round
+int decode_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t requested) {
     if (requested > 0) return requested;
     if (kv_len <= 0) return 1;
-    const int64_t rows = (int64_t)B * Hq;
+    const int64_t rows = (int64_t)B * Hq / decode_heads_per_wg(Hq, Hkv);
     int64_t want = (kTargetDecodeBlocks + rows - 1) / rows;
     const int64_t by_len = ((int64_t)kv_len + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
     if (want > by_len) want = by_len;
@@ -255,15 +264,17 @@ mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
     return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
 }
 
-int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t kv_len) {
-    if (B <= 0 || Hq <= 0 || kv_len < 0) return 0;
-    return decode_splits(B, Hq, kv_len, 0);
+int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || kv_len < 0) return 0;
+    return decode_splits(B, Hq, Hkv, kv_len, 0);
 }
 
-size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t kv_len, int32_t D, int32_t num_splits) {
-    if (B <= 0 || Hq <= 0 || kv_len < 0 || (D != 64 && D != 128) || num_splits < 0 || num_splits > kMaxSplits)
+size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t D,
+                                     int32_t num_splits) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || kv_len < 0 || (D != 64 && D != 128) ||
+        num_splits < 0 || num_splits > kMaxSplits)
         return 0;
-    const int splits = decode_splits(B, Hq, kv_len, num_splits);
+    const int splits = decode_splits(B, Hq, Hkv, kv_len, num_splits);
     return (size_t)B * Hq * splits * (size_t)(D + 2) * sizeof(float);
 }
 
@@ -284,9 +295,17 @@ mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
         return MM_ERR_STRIDE;
     if (strides_not_mult(a->q_strides, 2, 8) || strides_not_mult(a->kv_strides, 3, 8)) return MM_ERR_STRIDE;
     if (((uintptr_t)a->out & 1u) || ((uintptr_t)a->mask & 1u)) return MM_ERR_STRIDE;
+    int page_shift = 0;
+    if (a->block_table) {
+        if (a->page_size <= 0 || (a->page_size & (a->page_size - 1)) != 0) return MM_ERR_SHAPE;
+        if (a->block_table_stride < 0) return MM_ERR_STRIDE;
+        while ((1 << page_shift) < a->page_size) ++page_shift;
+        if ((int64_t)(a->Scap + a->page_size - 1) / a->page_size > a->block_table_stride && a->B > 1)
+            return MM_ERR_STRIDE;  // rows of the table would overlap
+    }
     if (a->B == 0) return MM_OK;
 
-    const int splits = decode_splits(a->B, a->Hq, a->kv_len, a->num_splits);
+    const int splits = decode_splits(a->B, a->Hq, a->Hkv, a->kv_len, a->num_splits);
     const size_t need = (size_t)a->B * a->Hq * splits * (size_t)(a->D + 2) * sizeof(float);
     if (!a->workspace || a->workspace_bytes < need) return MM_ERR_WORKSPACE;
     if (misaligned16(a->workspace)) return MM_ERR_WORKSPACE;
@@ -316,6 +335,10 @@ mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
     p.ws_o = ws;
     p.ws_m = ws + nrow * a->D;
     p.ws_l = p.ws_m + nrow;
+    p.heads_per_wg = decode_heads_per_wg(a->Hq, a->Hkv);
+    p.block_table = a->block_table;
+    p.bt_sb = a->block_table_stride;
+    p.page_shift = page_shift;
 
     const hipError_t e = launch_decode(p, a->dtype, a->D, (hipStream_t)stream);
     return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;

@@ -14,6 +14,8 @@
 //   pass 2 (merge): per (b, h) rescale the partials to the common max and normalise:
 //     O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, LSE = (M + log2 L) ln 2.
 // A row with no visible key (empty sequence or all -inf mask) yields O = 0, LSE = -inf.
+// With GQA a workgroup serves all (up to 8) query heads of a kv head, so each K/V byte
+// is read once; with a page table the K/V rows are gathered page by page.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,100 +57,130 @@ __device__ __forceinline__ float dot8(u32x4 q, u32x4 k, BF16) {
     return acc;
 }
 
-template <typename TT, int D, bool MASKED>
+// One workgroup = (split, group of G query heads sharing one kv head, batch). The G
+// heads' queries sit in registers, so each K/V byte is read from HBM once for all of
+// them (GQA); G = 1 is the plain per-head case. PAGED: key j of sequence b lives in
+// page block_table[b][j / page_size], row j % page_size, of the K/V page pools.
+template <typename TT, int D, bool MASKED, int G, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     constexpr int LPK = D / 8;       // lanes per key (16 bytes each)
     constexpr int KPW = 64 / LPK;    // keys per wave per step
     constexpr int NW = 4;
     constexpr int STEP = NW * KPW;   // keys per workgroup per step
-    constexpr int U = 8;             // steps in flight per iteration
-    constexpr int SLOTS = NW * KPW;  // partial softmax states per workgroup
+    constexpr int U = G <= 2 ? 8 : (G == 4 ? 4 : 2);  // steps in flight per iteration
+    constexpr int SLOTS = NW * KPW;  // partial softmax states per workgroup and head
 
     __shared__ float sm_m[SLOTS], sm_l[SLOTS];
     __shared__ __attribute__((aligned(16))) float sm_o[SLOTS][D];
 
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / LPK, c = lane % LPK;
     const int slot = wave * KPW + g;
-    const int hk = h / p.group;
+    const int h0 = hg * G;           // first query head of this workgroup
+    const int hk = h0 / p.group;     // G divides the group: one kv head for all G
 
     int len = p.kv_len;
     if (p.lens) len = min(max(p.lens[b], 0), p.kv_len);
     const int j_begin = s * p.chunk;
     const int j_end = min(len, j_begin + p.chunk);
 
-    const u32x4 qv = *(const u32x4 *)((const uint16_t *)p.q + b * p.q_sb + h * p.q_sh + 8 * c);
+    u32x4 qv[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+        qv[gi] = *(const u32x4 *)((const uint16_t *)p.q + b * p.q_sb + (h0 + gi) * p.q_sh + 8 * c);
     const float c2 = p.scale_log2;
 
-    const uint16_t *kbase = (const uint16_t *)p.k + b * p.kv_sb + hk * p.kv_sh + 8 * c;
-    const uint16_t *vbase = (const uint16_t *)p.v + b * p.kv_sb + hk * p.kv_sh + 8 * c;
-    const uint16_t *mbase = MASKED ? p.mask + b * p.m_sb + h * p.m_sh : nullptr;
+    // contiguous caches: [B, Hkv, S, D]; page pools: [pages, Hkv, page_size, D]
+    const uint16_t *kbase = (const uint16_t *)p.k + (PAGED ? 0 : b * p.kv_sb) + hk * p.kv_sh + 8 * c;
+    const uint16_t *vbase = (const uint16_t *)p.v + (PAGED ? 0 : b * p.kv_sb) + hk * p.kv_sh + 8 * c;
+    const int32_t *bt = PAGED ? p.block_table + b * p.bt_sb : nullptr;
+    auto key_off = [&](int j) -> int64_t {
+        if (!PAGED) return (int64_t)j * p.kv_ss;
+        return (int64_t)bt[j >> p.page_shift] * p.kv_sb + (int64_t)(j & ((1 << p.page_shift) - 1)) * p.kv_ss;
+    };
 
-    float m = -INFINITY, l = 0.f;
-    f32x8 o = {};
+    float m[G], l[G];
+    f32x8 o[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        m[gi] = -INFINITY;
+        l[gi] = 0.f;
+        o[gi] = f32x8{};
+    }
 
     for (int base = j_begin; base < j_end; base += STEP * U) {
         u32x4 kr[U], vr[U];
-        uint16_t mk[U];
+        uint16_t mk[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = min(base + u * STEP + slot, j_end - 1);  // tail lanes re-read a valid key
-            kr[u] = __builtin_nontemporal_load((const u32x4 *)(kbase + (int64_t)j * p.kv_ss));
-            vr[u] = __builtin_nontemporal_load((const u32x4 *)(vbase + (int64_t)j * p.kv_ss));
-            if (MASKED) mk[u] = mbase[j];
-        }
-        float t[U];
+            const int64_t off = key_off(j);
+            kr[u] = __builtin_nontemporal_load((const u32x4 *)(kbase + off));
+            vr[u] = __builtin_nontemporal_load((const u32x4 *)(vbase + off));
+            if (MASKED) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float dot = group_sum<LPK>(dot8(qv, kr[u], TT{})) * c2;
-            if (MASKED) dot = fmaf(widen1(mk[u], F16{}), kLog2e, dot);
-            t[u] = base + u * STEP + slot < j_end ? dot : -INFINITY;
-        }
-        float mt = t[0];
-#pragma unroll
-        for (int u = 1; u < U; ++u) mt = fmaxf(mt, t[u]);
-        const float m_new = fmaxf(m, mt);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        l *= alpha;
-        o *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float pv = fast_exp2(t[u] - m_use);
-            l += pv;
-            o += pv * widen8(vr[u], TT{});
-        }
-        m = m_new;
-    }
-
-    if (c == 0) {
-        sm_m[slot] = m;
-        sm_l[slot] = l;
-    }
-    *(f32x4 *)&sm_o[slot][8 * c] = f32x4{o[0], o[1], o[2], o[3]};
-    *(f32x4 *)&sm_o[slot][8 * c + 4] = f32x4{o[4], o[5], o[6], o[7]};
-    __syncthreads();
-
-    if (tid < D) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < SLOTS; ++k) M = fmaxf(M, sm_m[k]);
-        float Ls = 0.f, Od = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int k = 0; k < SLOTS; ++k) {
-                const float mk2 = sm_m[k];
-                const float w = mk2 == -INFINITY ? 0.f : fast_exp2(mk2 - M);
-                Ls += sm_l[k] * w;
-                Od += sm_o[k][tid] * w;
+                for (int gi = 0; gi < G; ++gi) mk[u][gi] = p.mask[b * p.m_sb + (h0 + gi) * p.m_sh + j];
             }
         }
-        const int64_t wi = ((int64_t)b * p.Hq + h) * p.splits + s;
-        p.ws_o[wi * D + tid] = Od;
-        if (tid == 0) {
-            p.ws_m[wi] = M;
-            p.ws_l[wi] = Ls;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            float t[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float dot = group_sum<LPK>(dot8(qv[gi], kr[u], TT{})) * c2;
+                if (MASKED) dot = fmaf(widen1(mk[u][gi], F16{}), kLog2e, dot);
+                t[u] = base + u * STEP + slot < j_end ? dot : -INFINITY;
+            }
+            float mt = t[0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, t[u]);
+            const float m_new = fmaxf(m[gi], mt);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fast_exp2(m[gi] - m_use);
+            l[gi] *= alpha;
+            o[gi] *= alpha;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float pv = fast_exp2(t[u] - m_use);
+                l[gi] += pv;
+                o[gi] += pv * widen8(vr[u], TT{});
+            }
+            m[gi] = m_new;
+        }
+    }
+
+    // combine the SLOTS partial states of each head (one head at a time through LDS)
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        if (gi > 0) __syncthreads();  // the previous head's reads are done
+        if (c == 0) {
+            sm_m[slot] = m[gi];
+            sm_l[slot] = l[gi];
+        }
+        *(f32x4 *)&sm_o[slot][8 * c] = f32x4{o[gi][0], o[gi][1], o[gi][2], o[gi][3]};
+        *(f32x4 *)&sm_o[slot][8 * c + 4] = f32x4{o[gi][4], o[gi][5], o[gi][6], o[gi][7]};
+        __syncthreads();
+        if (tid < D) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k) M = fmaxf(M, sm_m[k]);
+            float Ls = 0.f, Od = 0.f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int k = 0; k < SLOTS; ++k) {
+                    const float mk2 = sm_m[k];
+                    const float w = mk2 == -INFINITY ? 0.f : fast_exp2(mk2 - M);
+                    Ls += sm_l[k] * w;
+                    Od += sm_o[k][tid] * w;
+                }
+            }
+            const int64_t wi = ((int64_t)b * p.Hq + h0 + gi) * p.splits + s;
+            p.ws_o[wi * D + tid] = Od;
+            if (tid == 0) {
+                p.ws_m[wi] = M;
+                p.ws_l[wi] = Ls;
+            }
         }
     }
 }
@@ -205,14 +237,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     }
 }
 
+template <typename TT, int D, int G, bool PAGED>
+static hipError_t launch_split(const DecParams &p, hipStream_t s) {
+    const dim3 g1((unsigned)p.splits, (unsigned)(p.Hq / G), (unsigned)p.B);
+    if (p.mask)
+        decode_split_kernel<TT, D, true, G, PAGED><<<g1, dim3(256), 0, s>>>(p);
+    else
+        decode_split_kernel<TT, D, false, G, PAGED><<<g1, dim3(256), 0, s>>>(p);
+    return hipGetLastError();
+}
+
 template <typename TT, int D>
 static hipError_t launch_decode_t(const DecParams &p, hipStream_t s) {
-    const dim3 g1((unsigned)p.splits, (unsigned)p.Hq, (unsigned)p.B);
-    if (p.mask)
-        decode_split_kernel<TT, D, true><<<g1, dim3(256), 0, s>>>(p);
-    else
-        decode_split_kernel<TT, D, false><<<g1, dim3(256), 0, s>>>(p);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    const bool paged = p.block_table != nullptr;
+    switch (p.heads_per_wg) {
+        case 8: e = paged ? launch_split<TT, D, 8, true>(p, s) : launch_split<TT, D, 8, false>(p, s); break;
+        case 4: e = paged ? launch_split<TT, D, 4, true>(p, s) : launch_split<TT, D, 4, false>(p, s); break;
+        case 2: e = paged ? launch_split<TT, D, 2, true>(p, s) : launch_split<TT, D, 2, false>(p, s); break;
+        default: e = paged ? launch_split<TT, D, 1, true>(p, s) : launch_split<TT, D, 1, false>(p, s); break;
+    }
     if (e != hipSuccess) return e;
     decode_merge_kernel<TT, D><<<dim3((unsigned)p.Hq, (unsigned)p.B), dim3(256), 0, s>>>(p);
     return hipGetLastError();

@@ -68,6 +68,10 @@ struct DecParams {
     float *ws_o;           // [B, Hq, splits, D] unnormalised partial outputs
     float *ws_m;           // [B, Hq, splits] partial row max (base 2)
     float *ws_l;           // [B, Hq, splits] partial row sum
+    int heads_per_wg;      // query heads per split workgroup (1, 2, 4 or 8; divides group)
+    const int32_t *block_table;  // paged caches: [B, max_pages] page ids, or nullptr
+    int64_t bt_sb;         // block-table row stride (elements)
+    int page_shift;        // log2(page_size)
 };
 
 // Smallest number of query rows per forward workgroup (host-side grid bound).

@@ -173,3 +173,22 @@ def test_block_mask_create_rejects_before_launch(args, status):
 ])
 def test_fp8_args_rejected_before_launch(kw, status):
     assert _fwd(**kw) == status
+
+
+def test_decode_splits_count_head_groups():
+    """With GQA a split workgroup serves up to 8 query heads, so the automatic split
+    count targets the same number of workgroups with G times more splits."""
+    assert mm.decode_auto_splits(1, 32, 32768, Hkv=8) == 128      # group 4: 8 head groups
+    assert mm.decode_auto_splits(1, 32, 32768, Hkv=4) == 128      # group 8: 4 head groups, len bound
+    assert mm.decode_auto_splits(1, 32, 32768, Hkv=32) == 32
+    assert mm.decode_auto_splits(2, 24, 8192, Hkv=8) == 22        # group 3: one head per workgroup, ceil(1024/48)
+    assert mm.decode_workspace_size(1, 32, 32768, 128, Hkv=8) == 32 * 128 * 130 * 4
+    assert mm.load_library().mm_attn_decode_auto_splits(1, 32, 5, 100) == 0  # Hq % Hkv != 0
+
+
+@pytest.mark.parametrize("page_size,stride,status", [(12, 64, SHAPE), (0, 64, SHAPE), (16, -1, STRIDE),
+                                                     (16, 2, STRIDE)])
+def test_decode_rejects_bad_page_tables(page_size, stride, status):
+    # B = 2 with Scap = 128: 8 pages of 16 per sequence
+    assert _dec(B=2, Scap=128, kv_len=100, block_table=FAKE, page_size=page_size,
+                block_table_stride=stride) == status

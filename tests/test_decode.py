@@ -150,3 +150,66 @@ def test_workspace_reuse_across_calls_and_split_counts():
         o, l = mm.attn_decode(q, k, v, 3000, SCALE, mask=m, seq_lens=seq, num_splits=splits, workspace=ws)
         torch.cuda.synchronize()
         assert torch.allclose(o.float(), ref.float(), atol=2e-3) and torch.allclose(l, lref, atol=1e-5)
+
+
+# ------------------------------------------------------------ GQA head groups
+@pytest.mark.parametrize("Hq,Hkv", [(32, 16), (32, 8), (32, 4), (24, 8), (64, 4)])
+def test_gqa_head_groups(Hq, Hkv):
+    """Group sizes 2, 4, 8 (one workgroup per group), 3 (one head per workgroup) and 16
+    (two workgroups of 8 heads per kv head)."""
+    _run(2, Hq, Hkv, [2500, 777], 128, "f16", bias_seed=13, seed=13)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f16", 64), ("bf16", 128)])
+def test_gqa_dtypes(dtype, D):
+    _run(2, 16, 2, [1800, 4000], D, dtype, seed=14)
+
+
+# ------------------------------------------------------------ paged KV
+def _paged_run(B, Hq, Hkv, lens, D, dtype, page_size, *, seed=0, use_mask=True, num_splits=0):
+    import torch
+    import mask_mods_amd as mm
+    lens = np.asarray(lens, dtype=np.int64)
+    pages = -(-int(lens.max()) // page_size)
+    Scap = pages * page_size
+    print(f"[decode paged] B={B} Hq={Hq} Hkv={Hkv} lens={lens.tolist()} D={D} {dtype} page={page_size} "
+          f"splits={num_splits}", flush=True)
+    x = inputs.decode_inputs(seed, B, Hq, Hkv, lens, D, dtype, Scap=Scap, with_pad_mask=use_mask)
+    # scatter each sequence's logical pages to random physical pages of one pool (with
+    # a few unused pages between), and record the table
+    g = np.random.default_rng(seed + 7)
+    n_phys = B * pages + 5
+    perm = g.permutation(n_phys)[:B * pages].reshape(B, pages).astype(np.int32)
+    pool_k = np.zeros((n_phys, Hkv, page_size, D), dtype=x["k"].dtype)
+    pool_v = np.zeros_like(pool_k)
+    for b in range(B):
+        for pg in range(pages):
+            sl = slice(pg * page_size, (pg + 1) * page_size)
+            pool_k[perm[b, pg]] = x["k"][b, :, sl, :]
+            pool_v[perm[b, pg]] = x["v"][b, :, sl, :]
+    q = to_torch(x["q"], dtype)
+    kp, vp = to_torch(pool_k, dtype), to_torch(pool_v, dtype)
+    bt = torch.from_numpy(perm).cuda()
+    mask = to_torch(x["mask"], "f16") if use_mask else None
+    seq = torch.tensor(x["lens"], dtype=torch.int32, device="cuda")
+    out, lse = mm.attn_decode(q, kp, vp, int(lens.max()), SCALE, mask=mask, seq_lens=seq,
+                              block_table=bt, num_splits=num_splits)
+    torch.cuda.synchronize()
+    qd, kd, vd = (inputs.bits_to_f64(x[n], dtype) for n in ("q", "k", "v"))
+    md = inputs.bits_to_f64(x["mask"], "f16") if use_mask else None
+    O, L = oracle.attention(qd, kd, vd, scale=SCALE, Skv=int(lens.max()), add_mask=md, lens=x["lens"])
+    assert_parity(to_f64(out), O, O_ATOL, O_RTOL, "O")
+    assert_parity(to_f64(lse).reshape(B, Hq, 1), L, LSE_ATOL, LSE_RTOL, "LSE")
+
+
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+def test_paged(page_size):
+    _paged_run(3, 32, 32, [3000, 1, 1777], 128, "f16", page_size, seed=15)
+
+
+def test_paged_gqa_no_mask_forced_splits():
+    _paged_run(2, 32, 8, [4096, 333], 128, "bf16", 64, seed=16, use_mask=False, num_splits=7)
+
+
+def test_paged_long_and_empty():
+    _paged_run(2, 16, 16, [32768, 0], 64, "f16", 128, seed=17)
