@@ -60,6 +60,7 @@ def load():
         ctypes.c_double, ctypes.c_int, _dp,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
         _bp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        _ip, _ip, ctypes.c_int64, ctypes.c_int64,
         _dp, _dp, _dp,
     ]
     lib.oracle_attention_bwd.restype = ctypes.c_int
@@ -70,6 +71,7 @@ def load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
         _dp, ctypes.c_int64, _ip,
         _bp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        _ip, _ip, ctypes.c_int64, ctypes.c_int64,
         _lp, ctypes.c_int64, _dp, _dp, _dp, _dp,
     ]
     lib.oracle_attention.restype = ctypes.c_int
@@ -101,9 +103,20 @@ def _ptr(a, typ):
     return None if a is None else a.ctypes.data_as(typ)
 
 
+def _docs(q_doc, kv_doc, B, Sq, Skv):
+    """Document ids: None, or int [B, Sq] and int [B, Skv] (kv_doc defaults to q_doc)."""
+    if q_doc is None:
+        return None, None, 0, 0
+    kv_doc = q_doc if kv_doc is None else kv_doc
+    q_doc = np.ascontiguousarray(q_doc, dtype=np.int32).reshape(B, -1)
+    kv_doc = np.ascontiguousarray(kv_doc, dtype=np.int32).reshape(B, -1)
+    assert q_doc.shape[1] >= Sq and kv_doc.shape[1] >= Skv
+    return q_doc, kv_doc, q_doc.shape[1], kv_doc.shape[1]
+
+
 def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=False,
               slopes=None, rowdrop=None, add_mask=None, lens=None, rows=None, block_mask=None,
-              sensitivity=False):
+              q_doc=None, kv_doc=None, sensitivity=False):
     """Run the oracle.
 
     q: float64 [B,Hq,Sq,D]; k, v: float64 [B,Hkv,kv_cap,D] (first ``Skv`` keys used,
@@ -113,6 +126,8 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
     (b*Hq + h)*Sq + i (returns O [n,D], LSE [n]).
     block_mask: None or uint8 [B or 1, Hq or 1, ceil(Sq/128), ceil(Skv/64)] with
     0 = block masked, 1 = predicates decide, 2 = block kept (size-1 dims broadcast).
+    q_doc, kv_doc: None, or document ids [B, Sq] and [B, Skv]: a pair is kept only where
+    they are equal (kv_doc defaults to q_doc).
     sensitivity: also return wsq (per row, sum of squared weights) and wvar (per
     element, sum_j w_j^2 (V[j,d] - O[d])^2), shaped like LSE and O.
     """
@@ -151,6 +166,7 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
         assert Bb in (1, B) and Hb in (1, Hq)
         assert nqb >= -(-Sq // BLOCK_Q) and nkb >= -(-Skv // BLOCK_KV)
         bm_s = (0 if Bb == 1 else Hb * nqb * nkb, 0 if Hb == 1 else nqb * nkb, nkb)
+    qd_, kd_, qds, kds = _docs(q_doc, kv_doc, B, Sq, Skv)
     rc = load().oracle_attention(
         B, Hq, Hkv, Sq, Skv, D, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), kv_cap,
         float(scale), int(bool(alibi)), _ptr(slopes, _dp),
@@ -158,6 +174,7 @@ def attention(q, k, v, *, scale, Skv=None, causal=False, window=None, alibi=Fals
         seed & 0xFFFFFFFF, thr & 0xFFFFFFFF,
         _ptr(add_mask, _dp), mask_ld, _ptr(lens, _ip),
         _ptr(block_mask, _bp), bm_s[0], bm_s[1], bm_s[2],
+        _ptr(qd_, _ip), _ptr(kd_, _ip), qds, kds,
         _ptr(rows, _lp), n if rows is not None else 0, _ptr(out, _dp), _ptr(lse, _dp),
         _ptr(wsq, _dp), _ptr(wvar, _dp))
     if rc != 0:
@@ -196,7 +213,7 @@ def block_classes(Sq: int, Skv: int, *, causal: bool = False, window=None) -> np
 
 
 def attention_bwd(q, k, v, dout, *, scale, causal=False, window=None, alibi=False, slopes=None,
-                  rowdrop=None, block_mask=None):
+                  rowdrop=None, block_mask=None, q_doc=None, kv_doc=None):
     """Gradients (dq, dk, dv) of sum(dout * O) for the forward of ``attention`` (no
     additive mask or lengths), in float64. Shapes as ``attention`` with kv_cap = Skv."""
     q = np.ascontiguousarray(q, dtype=np.float64)
@@ -219,12 +236,14 @@ def attention_bwd(q, k, v, dout, *, scale, causal=False, window=None, alibi=Fals
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    qd_, kd_, qds, kds = _docs(q_doc, kv_doc, B, Sq, Skv)
     rc = load().oracle_attention_bwd(
         B, Hq, Hkv, Sq, Skv, D, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(dout, _dp),
         float(scale), int(bool(alibi)), _ptr(slopes, _dp),
         int(bool(causal)), -1 if window is None else int(window), int(rowdrop is not None),
         seed & 0xFFFFFFFF, thr & 0xFFFFFFFF,
         _ptr(block_mask, _bp), bm_s[0], bm_s[1], bm_s[2],
+        _ptr(qd_, _ip), _ptr(kd_, _ip), qds, kds,
         _ptr(dq, _dp), _ptr(dk, _dp), _ptr(dv, _dp))
     if rc != 0:
         raise ValueError("oracle_attention_bwd rejected its arguments")

@@ -33,6 +33,9 @@
  *                    Austin Appleby's MurmurHash3 (public domain).
  * alibi slope for query head h of H: 2^(-8(h+1)/H) unless slopes are given.
  *
+ * Document mask (optional, a mask_mod that captures tensors): keep iff
+ * q_doc[b][i] == kv_doc[b][j], AND-composed with the other predicates.
+ *
  * Block mask (optional, BlockMask-style): one byte per (b, h, q block of 128 rows,
  * kv block of 64 keys): 0 = no pair of the block is kept; 2 = every pair is kept and
  * the mask_mod predicates (causal, window) are not evaluated there; 1 = the predicates
@@ -105,6 +108,8 @@ typedef struct {
     const int32_t *lens;
     const uint8_t *block_mask;
     int64_t bm_sb, bm_sh, bm_sq;
+    const int32_t *q_doc, *kv_doc;  /* document ids per position, or NULL */
+    int64_t q_doc_sb, kv_doc_sb;
 } problem;
 
 #define ORACLE_BLOCK_Q 128
@@ -134,6 +139,7 @@ static double row_scores(const problem *p, int b, int h, int i, double *s)
         if (blk == 1) {
             if (p->causal && !(j <= i)) keep = 0;
             if (p->window >= 0 && !(abs(i - j) <= p->window)) keep = 0;
+            if (p->q_doc && p->q_doc[b * p->q_doc_sb + i] != p->kv_doc[b * p->kv_doc_sb + j]) keep = 0;
         }
         if (!keep) {
             s[j] = -INFINITY;
@@ -213,6 +219,7 @@ int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                      int causal, int window, int rowdrop, uint32_t seed, uint32_t threshold,
                      const double *add_mask, int64_t mask_ld, const int32_t *lens,
                      const uint8_t *block_mask, int64_t bm_sb, int64_t bm_sh, int64_t bm_sq,
+                     const int32_t *q_doc, const int32_t *kv_doc, int64_t q_doc_sb, int64_t kv_doc_sb,
                      const int64_t *rows, int64_t nrows, double *out, double *lse,
                      double *wsq, double *wvar)
 {
@@ -221,9 +228,10 @@ int oracle_attention(int B, int Hq, int Hkv, int Sq, int Skv, int D,
     if (!q || !k || !v || !out || !lse) return -1;
     const int64_t total = (int64_t)B * Hq * Sq;
     if (!rows) nrows = total;
+    if ((q_doc == NULL) != (kv_doc == NULL)) return -1;
     problem p = {B, Hq, Hkv, Sq, Skv, D, kv_cap, q, k, v, scale, alibi, slopes,
                  causal, window, rowdrop, seed, threshold, add_mask, mask_ld, lens,
-                 block_mask, bm_sb, bm_sh, bm_sq};
+                 block_mask, bm_sb, bm_sh, bm_sq, q_doc, kv_doc, q_doc_sb, kv_doc_sb};
     int bad = 0;
 #pragma omp parallel
     {
@@ -271,14 +279,16 @@ int oracle_attention_bwd(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                          double scale, int alibi, const double *slopes,
                          int causal, int window, int rowdrop, uint32_t seed, uint32_t threshold,
                          const uint8_t *block_mask, int64_t bm_sb, int64_t bm_sh, int64_t bm_sq,
+                         const int32_t *q_doc, const int32_t *kv_doc, int64_t q_doc_sb, int64_t kv_doc_sb,
                          double *dq, double *dk, double *dv)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return -1;
     if (Hq % Hkv != 0) return -1;
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    if ((q_doc == NULL) != (kv_doc == NULL)) return -1;
     problem p = {B, Hq, Hkv, Sq, Skv, D, Skv, q, k, v, scale, alibi, slopes,
                  causal, window, rowdrop, seed, threshold, NULL, 0, NULL,
-                 block_mask, bm_sb, bm_sh, bm_sq};
+                 block_mask, bm_sb, bm_sh, bm_sq, q_doc, kv_doc, q_doc_sb, kv_doc_sb};
     const int group = Hq / Hkv;
     int bad = 0;
 #pragma omp parallel

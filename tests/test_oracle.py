@@ -27,7 +27,7 @@ def _f64(x, dtype):
 
 
 def brute(q, k, v, scale, causal=False, window=None, slopes=None, add_mask=None,
-          lens=None, dropped=None, Skv=None):
+          lens=None, dropped=None, Skv=None, q_doc=None, kv_doc=None):
     """Full-matrix attention in float64 with library softmax pieces."""
     B, Hq, Sq, D = q.shape
     Hkv = k.shape[1]
@@ -54,6 +54,8 @@ def brute(q, k, v, scale, causal=False, window=None, slopes=None, add_mask=None,
         keep &= (j[None] < np.asarray(lens)[:, None, None])[:, None]
     if dropped is not None:
         keep &= ~dropped[..., None]
+    if q_doc is not None:
+        keep &= (np.asarray(q_doc)[:, :, None] == np.asarray(kv_doc)[:, None, :])[:, None]
     S = np.where(keep, S, -np.inf)
     with np.errstate(invalid="ignore", divide="ignore"):
         lse = logsumexp(S, axis=-1)
@@ -577,3 +579,66 @@ def test_sensitivity_fully_masked_rows_are_zero():
     _, L, wsq, wvar = oracle.attention(q, k, v, scale=0.3, causal=True, window=3, sensitivity=True)
     dead = ~np.isfinite(L)
     assert dead.any() and np.all(wsq[dead] == 0) and np.all(wvar[dead] == 0)
+
+
+# ------------------------------------------------ document mask (a tensor-capturing mask_mod)
+def _packed_docs(g, B, S, n_docs):
+    """Non-decreasing document ids: n_docs random lengths per sequence."""
+    out = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        cuts = np.sort(g.choice(np.arange(1, S), size=n_docs - 1, replace=False))
+        out[b] = np.searchsorted(cuts, np.arange(S), side="right")
+    return out
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 5)])
+def test_document_mask_vs_brute_force(causal, window):
+    B, Hq, Hkv, S, D = 2, 4, 2, 40, 8
+    x = inputs.attention_inputs(12, B, Hq, Hkv, S, S, D, "f32")
+    q, k, v = (_f64(x[n], "f32") for n in ("q", "k", "v"))
+    docs = _packed_docs(np.random.default_rng(1), B, S, 4)
+    O, L = oracle.attention(q, k, v, scale=0.3, causal=causal, window=window, q_doc=docs)
+    Ob, Lb = brute(q, k, v, 0.3, causal, window, q_doc=docs, kv_doc=docs)
+    close(O, Ob, 1e-11)
+    close(L, Lb, 1e-11)
+
+
+def test_document_mask_cross_attention_vs_brute_force():
+    B, H, Sq, Skv, D = 1, 2, 17, 29, 4
+    x = inputs.attention_inputs(13, B, H, H, Sq, Skv, D, "f32")
+    q, k, v = (_f64(x[n], "f32") for n in ("q", "k", "v"))
+    g = np.random.default_rng(2)
+    qd, kd = _packed_docs(g, B, Sq, 3), _packed_docs(g, B, Skv, 3)
+    O, L = oracle.attention(q, k, v, scale=0.5, q_doc=qd, kv_doc=kd)
+    Ob, Lb = brute(q, k, v, 0.5, q_doc=qd, kv_doc=kd)
+    close(O, Ob, 1e-11)
+    close(L, Lb, 1e-11)
+
+
+def test_document_mask_closed_form_counts():
+    """Q = 0, causal: row i keeps the keys of its own document up to i: LSE = ln(i - start + 1)."""
+    S = 30
+    q, k, v = _zero_q(1, 1, 1, S, S, 3)
+    docs = np.array([[0] * 7 + [1] * 12 + [2] * 11], dtype=np.int32)
+    _, L = oracle.attention(q, k, v, scale=1.0, causal=True, q_doc=docs)
+    starts = {0: 0, 1: 7, 2: 19}
+    for i in range(S):
+        assert L[0, 0, i] == pytest.approx(math.log(i - starts[int(docs[0, i])] + 1), abs=1e-14)
+
+
+def test_document_mask_invariants():
+    q, k, v = _rand(1, 2, 2, 50, 50, 8)
+    one = np.zeros((1, 50), dtype=np.int32)
+    O0, L0 = oracle.attention(q, k, v, scale=0.4, causal=True)
+    O1, L1 = oracle.attention(q, k, v, scale=0.4, causal=True, q_doc=one)
+    np.testing.assert_array_equal(O0, O1)
+    np.testing.assert_array_equal(L0, L1)
+    # every position its own document, causal: only the diagonal -> O = V row, LSE = score
+    ids = np.arange(50, dtype=np.int32)[None]
+    O2, _ = oracle.attention(q, k, v, scale=0.4, causal=True, q_doc=ids)
+    np.testing.assert_allclose(O2, v, atol=1e-14)
+    # full blocks bypass the document predicate like the others
+    bm = np.full((1, 1, 1, 1), 2, dtype=np.uint8)
+    O3, L3 = oracle.attention(q, k, v, scale=0.4, q_doc=ids, block_mask=bm)
+    O4, L4 = oracle.attention(q, k, v, scale=0.4)
+    np.testing.assert_array_equal(O3, O4)

@@ -50,6 +50,17 @@ CASES = {
 }
 
 
+def test_document_mask_matches_finite_differences():
+    B, Hq, Hkv, S, D = 1, 2, 1, 9, 3
+    q, k, v, do = _inputs(B, Hq, Hkv, S, S, D, seed=9)
+    docs = np.array([[0, 0, 0, 1, 1, 2, 2, 2, 2]], dtype=np.int32)
+    kw = dict(scale=0.45, causal=True, q_doc=docs)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, **kw)
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = _finite_diff(x, lambda: _loss(q, k, v, do, kw))
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-7)
+
+
 @pytest.mark.parametrize("case", sorted(CASES))
 @pytest.mark.parametrize("shape", [(1, 2, 2, 6, 6, 4), (1, 4, 2, 5, 7, 3), (2, 2, 1, 7, 4, 4)])
 def test_matches_finite_differences(case, shape):

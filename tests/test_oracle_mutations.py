@@ -34,6 +34,8 @@ MUTANTS = {
     "full_block_predicated": ("if (blk == 1) {", "if (blk != 0) {"),
     "block_kv_size": ("j / ORACLE_BLOCK_KV];", "j / ORACLE_BLOCK_Q];"),
     "block_empty_kept": ("if (blk == 0) keep = 0;", "if (blk == 3) keep = 0;"),
+    "doc_order": ("p->q_doc[b * p->q_doc_sb + i] != p->kv_doc[b * p->kv_doc_sb + j]",
+                  "p->q_doc[b * p->q_doc_sb + i] < p->kv_doc[b * p->kv_doc_sb + j]"),
 }
 
 
