@@ -73,9 +73,15 @@ enum {
     MM_MASK_NONE = 0u,
     MM_MASK_CAUSAL = 1u,  /* keep iff kv_idx <= q_idx                                  */
     MM_MASK_WINDOW = 2u,  /* keep iff |q_idx - kv_idx| <= window (inclusive)           */
-    MM_MASK_ROWDROP = 4u  /* drop the whole row iff fmix32(seed ^ row) < threshold,
+    MM_MASK_ROWDROP = 4u, /* drop the whole row iff fmix32(seed ^ row) < threshold,
                              row = (b*Hq + h)*Sq + q_idx; fmix32 = MurmurHash3's
                              32-bit finalizer                                           */
+    MM_MASK_DOCUMENT = 8u /* keep iff q_doc_ids[b][q_idx] == kv_doc_ids[b][kv_idx]: a
+                             mask_mod that captures tensors (packed documents). The ids
+                             must not decrease along the positions of a sequence (the
+                             kernels skip whole tiles from the end ids). Composes with
+                             MM_MASK_CAUSAL, MM_MASK_ROWDROP and the block mask; not
+                             with MM_MASK_WINDOW (MM_ERR_UNSUPPORTED)                   */
 };
 
 /*
@@ -83,7 +89,7 @@ enum {
  * shape of PyTorch's BlockMask with its full and partial block lists): one byte per
  * (b, h, query block of MM_BLOCK_Q rows, key block of MM_BLOCK_KV keys):
  *   0        no pair of the block is kept; its keys are never read,
- *   1        partial: the mask_mod predicates (causal, window) decide per pair,
+ *   1        partial: the mask_mod predicates (causal, window, document) decide per pair,
  *   2        full: every pair is kept and the predicates are not evaluated.
  * Other values are reserved and currently act as 2. MM_MASK_ROWDROP and the key-length
  * bound apply in every block. Byte (b, h, qb, kb) sits at
@@ -103,6 +109,9 @@ typedef struct mm_mods {
     const float *alibi_slopes;    /* device fp32 [Hq], or NULL for 2^(-8(h+1)/Hq)      */
     const uint8_t *block_mask;    /* device block mask (above), or NULL for none       */
     int64_t block_mask_strides[3];/* elements (bytes), for b, h, query block; >= 0     */
+    const int32_t *q_doc_ids;     /* MM_MASK_DOCUMENT: device int32 [B, >= Sq]          */
+    const int32_t *kv_doc_ids;    /* MM_MASK_DOCUMENT: device int32 [B, >= Skv]         */
+    int64_t doc_strides[2];       /* elements between sequences of q / kv ids; >= 0    */
 } mm_mods;
 
 typedef struct mm_fwd_args {

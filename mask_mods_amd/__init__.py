@@ -30,7 +30,7 @@ _LIB_PATH = os.environ.get("MASKMODS_LIB") or os.path.join(_PKG, "libmaskmods.so
 
 MM_F32, MM_F16, MM_BF16, MM_FP8_E4M3 = 0, 1, 2, 3
 SCORE_NONE, SCORE_ALIBI = 0, 1
-MASK_CAUSAL, MASK_WINDOW, MASK_ROWDROP = 1, 2, 4
+MASK_CAUSAL, MASK_WINDOW, MASK_ROWDROP, MASK_DOCUMENT = 1, 2, 4, 8
 ROWDROP_5PCT = int(0.05 * 2 ** 32)  # threshold that drops ~5% of rows
 # block mask: query rows x keys per block, and the per-block classes
 BLOCK_Q, BLOCK_KV = 128, 64
@@ -58,6 +58,9 @@ class _Mods(ctypes.Structure):
         ("alibi_slopes", ctypes.c_void_p),
         ("block_mask", ctypes.c_void_p),
         ("block_mask_strides", ctypes.c_int64 * 3),
+        ("q_doc_ids", ctypes.c_void_p),
+        ("kv_doc_ids", ctypes.c_void_p),
+        ("doc_strides", ctypes.c_int64 * 2),
     ]
 
 
@@ -203,8 +206,8 @@ def _check_dev(*ts):
 
 
 def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_slopes=None,
-             mask_flags=0, window=None, rowdrop=None, block_mask=None, descale=None,
-             return_lse=True, out=None, lse=None):
+             mask_flags=0, window=None, rowdrop=None, block_mask=None, q_doc=None, kv_doc=None,
+             descale=None, return_lse=True, out=None, lse=None):
     """Fused attention forward.
 
     q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (bf16, f16, f32 or float8_e4m3fn; D in {64,128}).
@@ -217,11 +220,14 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
     one class per (query block of BLOCK_Q rows, key block of BLOCK_KV keys):
     BLOCK_EMPTY (skipped), BLOCK_PARTIAL (the mask predicates decide) or BLOCK_FULL
     (all kept); size-1 leading dims broadcast.
+    q_doc, kv_doc: document mask, int32 device tensors [B|1, >=Sq] and [B|1, >=Skv] of
+    ids that do not decrease along the sequence (kv_doc defaults to q_doc): a pair is
+    kept only where the two ids are equal. Not combinable with ``window``.
     Returns (out, lse) with lse fp32 [B,Hq,Sq] (None if return_lse is False).
     """
     torch = _torch()
     lib = load_library()
-    dev = _check_dev(q, k, v, out, lse, alibi_slopes, block_mask)
+    dev = _check_dev(q, k, v, out, lse, alibi_slopes, block_mask, q_doc, kv_doc)
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
     if v.shape != k.shape or Bk != B or Dk != D or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -236,31 +242,6 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (B, Hq, Sq)):
         raise ValueError("lse must be contiguous fp32 [B,Hq,Sq]")
-    if isinstance(score_mod, str):
-        score_mod = {"none": SCORE_NONE, "alibi": SCORE_ALIBI}[score_mod]
-    flags = int(mask_flags)
-    if window is not None:
-        flags |= MASK_WINDOW
-    seed, thr = 0, 0
-    if rowdrop is not None:
-        flags |= MASK_ROWDROP
-        seed, thr = rowdrop
-    if alibi_slopes is not None:
-        if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (Hq,) \
-                or not alibi_slopes.is_contiguous():
-            raise ValueError("alibi_slopes must be contiguous fp32 [Hq]")
-    bm_strides = (0, 0, 0)
-    if block_mask is not None:
-        nqb, nkb = -(-Sq // BLOCK_Q), -(-Skv // BLOCK_KV)
-        if block_mask.dtype != torch.uint8 or block_mask.dim() != 4:
-            raise ValueError("block_mask must be a 4-D uint8 tensor")
-        bb, bh, bq, bk = block_mask.shape
-        if bb not in (1, B) or bh not in (1, Hq) or bq < nqb or bk < nkb:
-            raise ValueError(f"block_mask shape {tuple(block_mask.shape)} does not cover "
-                             f"[{B}|1, {Hq}|1, {nqb}, {nkb}]")
-        if bk > 1 and block_mask.stride(3) != 1:
-            raise ValueError("block_mask's last dimension must be contiguous")
-        bm_strides = tuple(0 if n == 1 else st for n, st in zip(block_mask.shape[:3], block_mask.stride()[:3]))
     a = FwdArgs()
     a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
@@ -272,15 +253,9 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
     a.o_strides = _I64x3(*out.stride()[:3])
     a.scale = float(scale)
     a.causal = 1 if causal else 0
-    a.mods.score_mod = int(score_mod)
-    a.mods.mask_flags = flags
-    a.mods.window = int(window) if window is not None else 0
-    a.mods.rowdrop_seed = seed & 0xFFFFFFFF
-    a.mods.rowdrop_threshold = thr & 0xFFFFFFFF
-    a.mods.alibi_slopes = alibi_slopes.data_ptr() if alibi_slopes is not None else None
+    a.mods = _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, Sq, Skv, B,
+                   q_doc, kv_doc)
     a.descale_q, a.descale_k, a.descale_v = (1.0, 1.0, 1.0) if descale is None else map(float, descale)
-    a.mods.block_mask = block_mask.data_ptr() if block_mask is not None and block_mask.numel() else None
-    a.mods.block_mask_strides = _I64x3(*bm_strides)
     st = lib.mm_attn_fwd(ctypes.byref(a), _stream_ptr(dev))
     if st != 0:
         raise MaskModsError(st, "mm_attn_fwd")
@@ -311,7 +286,8 @@ def block_mask_create(Sq, Skv, *, causal=False, window=None, device=None, out=No
     return out
 
 
-def _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, Sq, Skv, B):
+def _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, Sq, Skv, B,
+          q_doc=None, kv_doc=None):
     """Fill an mm_mods struct (shared by the forward and backward calls)."""
     torch = _torch()
     m = _Mods()
@@ -348,6 +324,18 @@ def _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, 
     m.alibi_slopes = alibi_slopes.data_ptr() if alibi_slopes is not None else None
     m.block_mask = block_mask.data_ptr() if block_mask is not None and block_mask.numel() else None
     m.block_mask_strides = _I64x3(*bm_strides)
+    if kv_doc is not None and q_doc is None:
+        raise ValueError("kv_doc needs q_doc")
+    if q_doc is not None:
+        kv_doc = q_doc if kv_doc is None else kv_doc
+        for name, t, n in (("q_doc", q_doc, Sq), ("kv_doc", kv_doc, Skv)):
+            if t.dtype != torch.int32 or t.dim() != 2 or t.shape[0] not in (1, B) or t.shape[1] < n:
+                raise ValueError(f"{name} must be int32 [{B}|1, >={n}], got {t.dtype} {tuple(t.shape)}")
+        m.mask_flags = flags | MASK_DOCUMENT
+        m.q_doc_ids = q_doc.data_ptr() if q_doc.numel() else None
+        m.kv_doc_ids = kv_doc.data_ptr() if kv_doc.numel() else None
+        m.doc_strides = _I64x2(0 if q_doc.shape[0] == 1 else q_doc.stride(0),
+                               0 if kv_doc.shape[0] == 1 else kv_doc.stride(0))
     return m
 
 
@@ -357,7 +345,7 @@ def bwd_workspace_size(B, Hq, Sq) -> int:
 
 def attn_bwd(q, k, v, out, lse, dout, scale=None, *, causal=False, score_mod=SCORE_NONE,
              alibi_slopes=None, mask_flags=0, window=None, rowdrop=None, block_mask=None,
-             workspace=None, dq=None, dk=None, dv=None):
+             q_doc=None, kv_doc=None, workspace=None, dq=None, dk=None, dv=None):
     """Backward of attn_fwd: gradients (dq, dk, dv) of sum(dout * out).
 
     q, k, v, out, lse: the forward's inputs and outputs (lse is required); dout like out.
@@ -365,7 +353,7 @@ def attn_bwd(q, k, v, out, lse, dout, scale=None, *, causal=False, score_mod=SCO
     """
     torch = _torch()
     lib = load_library()
-    dev = _check_dev(q, k, v, out, lse, dout, alibi_slopes, block_mask, workspace, dq, dk, dv)
+    dev = _check_dev(q, k, v, out, lse, dout, alibi_slopes, block_mask, q_doc, kv_doc, workspace, dq, dk, dv)
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
     if v.shape != k.shape or Bk != B or Dk != D or out.shape != q.shape or dout.shape != q.shape:
@@ -392,7 +380,8 @@ def attn_bwd(q, k, v, out, lse, dout, scale=None, *, causal=False, score_mod=SCO
         setattr(a, name + "_strides", _I64x3(*t.stride()[:3]))
     a.scale = float(scale)
     a.causal = 1 if causal else 0
-    a.mods = _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, Sq, Skv, B)
+    a.mods = _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, Sq, Skv, B,
+                   q_doc, kv_doc)
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib.mm_attn_bwd(ctypes.byref(a), _stream_ptr(dev))

@@ -31,6 +31,17 @@ bool strides_not_mult(const int64_t *s, int n, int m) {
     return false;
 }
 
+// The document mask's id arrays: both present (when any pair exists), 4-byte aligned,
+// non-negative strides; not composed with the window.
+mm_status check_doc(const mm_mods &m, bool pairs) {
+    if (!(m.mask_flags & MM_MASK_DOCUMENT)) return MM_OK;
+    if (m.mask_flags & MM_MASK_WINDOW) return MM_ERR_UNSUPPORTED;
+    if (pairs && (!m.q_doc_ids || !m.kv_doc_ids)) return MM_ERR_NULL;
+    if (bad_strides(m.doc_strides, 2)) return MM_ERR_STRIDE;
+    if (((uintptr_t)m.q_doc_ids | (uintptr_t)m.kv_doc_ids) & 3u) return MM_ERR_STRIDE;
+    return MM_OK;
+}
+
 // query heads per split workgroup: the largest of 8, 4, 2, 1 dividing the GQA group
 int decode_heads_per_wg(int32_t Hq, int32_t Hkv) {
     const int group = Hq / Hkv;
@@ -56,7 +67,7 @@ int decode_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t re
 
 extern "C" {
 
-int32_t mm_version(void) { return 200; }
+int32_t mm_version(void) { return 400; }
 
 size_t mm_fwd_args_size(void) { return sizeof(mm_fwd_args); }
 size_t mm_decode_args_size(void) { return sizeof(mm_decode_args); }
@@ -92,10 +103,11 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
     if (a->Hq % a->Hkv != 0) return MM_ERR_SHAPE;
     if (a->D != 64 && a->D != 128) return MM_ERR_UNSUPPORTED;
     if (a->mods.score_mod != MM_SCORE_NONE && a->mods.score_mod != MM_SCORE_ALIBI) return MM_ERR_UNSUPPORTED;
-    if (a->mods.mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW | MM_MASK_ROWDROP))
+    if (a->mods.mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW | MM_MASK_ROWDROP | MM_MASK_DOCUMENT))
         return MM_ERR_UNSUPPORTED;
     if ((a->mods.mask_flags & MM_MASK_WINDOW) && a->mods.window < 0) return MM_ERR_SHAPE;
     if (a->mods.block_mask && bad_strides(a->mods.block_mask_strides, 3)) return MM_ERR_STRIDE;
+    if (const mm_status ds = check_doc(a->mods, !no_rows && (int64_t)a->B * a->Skv != 0)) return ds;
     if (!isfinite(a->scale)) return MM_ERR_SHAPE;
     if (bad_strides(a->q_strides, 3) || bad_strides(a->k_strides, 3) || bad_strides(a->v_strides, 3) ||
         bad_strides(a->o_strides, 3))
@@ -155,6 +167,12 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
     if (a->causal || (a->mods.mask_flags & MM_MASK_CAUSAL)) mask |= MASK_CAUSAL;
     if (a->mods.mask_flags & MM_MASK_WINDOW) mask |= MASK_WINDOW;
     if (a->mods.block_mask) mask |= MASK_BLOCK;
+    // with no keys there is nothing to mask (and the ids may be absent)
+    if ((a->mods.mask_flags & MM_MASK_DOCUMENT) && a->Skv > 0) mask |= MASK_DOC;
+    p.qdoc = a->mods.q_doc_ids;
+    p.kvdoc = a->mods.kv_doc_ids;
+    p.qdoc_sb = a->mods.doc_strides[0];
+    p.kvdoc_sb = a->mods.doc_strides[1];
     const bool alibi = a->mods.score_mod == MM_SCORE_ALIBI;
     hipStream_t s = (hipStream_t)stream;
 
@@ -205,10 +223,11 @@ mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
     if (rows && (!a->q || !a->out || !a->dout || !a->lse || !a->dq)) return MM_ERR_NULL;
     if (keys && (!a->k || !a->v || !a->dk || !a->dv)) return MM_ERR_NULL;
     if (a->mods.score_mod != MM_SCORE_NONE && a->mods.score_mod != MM_SCORE_ALIBI) return MM_ERR_UNSUPPORTED;
-    if (a->mods.mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW | MM_MASK_ROWDROP))
+    if (a->mods.mask_flags & ~(uint32_t)(MM_MASK_CAUSAL | MM_MASK_WINDOW | MM_MASK_ROWDROP | MM_MASK_DOCUMENT))
         return MM_ERR_UNSUPPORTED;
     if ((a->mods.mask_flags & MM_MASK_WINDOW) && a->mods.window < 0) return MM_ERR_SHAPE;
     if (a->mods.block_mask && bad_strides(a->mods.block_mask_strides, 3)) return MM_ERR_STRIDE;
+    if (const mm_status ds = check_doc(a->mods, rows && keys)) return ds;
     if (!isfinite(a->scale)) return MM_ERR_SHAPE;
     const int64_t *st[8] = {a->q_strides, a->k_strides, a->v_strides, a->o_strides,
                             a->do_strides, a->dq_strides, a->dk_strides, a->dv_strides};
@@ -258,6 +277,12 @@ mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
     if (a->causal || (a->mods.mask_flags & MM_MASK_CAUSAL)) mask |= MASK_CAUSAL;
     if (a->mods.mask_flags & MM_MASK_WINDOW) mask |= MASK_WINDOW;
     if (a->mods.block_mask) mask |= MASK_BLOCK;
+    // without rows or keys there is no pair to mask (and the ids may be absent)
+    if ((a->mods.mask_flags & MM_MASK_DOCUMENT) && rows && keys) mask |= MASK_DOC;
+    p.qdoc = a->mods.q_doc_ids;
+    p.kvdoc = a->mods.kv_doc_ids;
+    p.qdoc_sb = a->mods.doc_strides[0];
+    p.kvdoc_sb = a->mods.doc_strides[1];
     // the row-drop mod needs nothing here: dropped rows have LSE = -inf
     const hipError_t e = launch_bwd(p, a->dtype, a->D, a->mods.score_mod == MM_SCORE_ALIBI, mask,
                                     (hipStream_t)stream);

@@ -108,6 +108,19 @@ void bwd_dq_kernel(BwdParams p) {
         j_lo = max(0, q0 - p.window);
         if (!(MASK & MASK_CAUSAL)) j_hi = min(j_hi, row_max + p.window + 1);
     }
+    // packed documents: keys of the documents of the tile's rows; per wave, the document
+    // ids of its first and last rows and, per lane, of its row
+    int wd_lo = 0, wd_hi = 0, mydoc = 0;
+    if (MASK & MASK_DOC) {
+        const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
+        if (!(MASK & MASK_BLOCK)) {
+            j_lo = max(j_lo, doc_lower(kd, p.Skv, qd[q0]));
+            j_hi = min(j_hi, doc_upper(kd, p.Skv, qd[row_max]));
+        }
+        wd_lo = qd[min(r0, p.Sq - 1)];
+        wd_hi = qd[min(r0 + 31, p.Sq - 1)];
+        mydoc = qd[min(row, p.Sq - 1)];
+    }
     const int kt_lo = j_lo / BN;
     const int kt_hi = j_hi > j_lo ? (j_hi + BN - 1) / BN : kt_lo;
 
@@ -182,6 +195,12 @@ void bwd_dq_kernel(BwdParams p) {
             skip |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
+        if ((MASK & MASK_DOC) && pred && !skip) {
+            const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
+            const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
+            skip |= kdh < wd_lo || kdl > wd_hi;
+            need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
+        }
         if (skip) return;
         // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T, then dS^T, then
         // dQ^T += K^T dS^T over the block's two 16-key k-steps
@@ -214,6 +233,8 @@ void bwd_dq_kernel(BwdParams p) {
                             bool keep = j < p.Skv;
                             if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
                             if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                            if ((MASK & MASK_DOC) && pred)
+                                keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
                             pv = keep ? fast_exp2(t - lse2) : 0.f;
                         } else {
                             pv = fast_exp2(fmaf(sacc[e], c2, -lse2));
@@ -344,6 +365,19 @@ void bwd_dkdv_kernel(BwdParams p) {
         i_hi = min(i_hi, kmax + p.window + 1);
         if (!(MASK & MASK_CAUSAL)) i_lo = max(0, kmin - p.window);
     }
+    // packed documents: rows of the documents of the tile's keys; per wave, the document
+    // ids of its first and last keys and, per lane, of its key
+    int wk_lo = 0, wk_hi = 0, mykdoc = 0;
+    if ((MASK & MASK_DOC) && p.Skv > 0) {
+        const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
+        if (!(MASK & MASK_BLOCK)) {
+            i_lo = max(i_lo, doc_lower(qd, p.Sq, kd[kmin]));
+            i_hi = min(i_hi, doc_upper(qd, p.Sq, kd[kmax]));
+        }
+        wk_lo = kd[min(kw0, p.Skv - 1)];
+        wk_hi = kd[min(kw0 + 31, p.Skv - 1)];
+        mykdoc = kd[min(key, p.Skv - 1)];
+    }
     const int qt_lo = i_lo / BQ;
     const int qt_hi = i_hi > i_lo ? (i_hi + BQ - 1) / BQ : qt_lo;
     const int nq = qt_hi - qt_lo;
@@ -434,6 +468,12 @@ void bwd_dkdv_kernel(BwdParams p) {
             skip |= (kw0 - i_last > p.window) || (i0 - (kw0 + 31) > p.window);
             need_mask |= max(i_last - kw0, kw0 + 31 - i0) > p.window;
         }
+        if ((MASK & MASK_DOC) && pred && !skip) {
+            const int32_t *qd = p.qdoc + b * p.qdoc_sb;
+            const int qdl = qd[i0], qdh = qd[min(i_last, p.Sq - 1)];
+            skip |= qdh < wk_lo || qdl > wk_hi;
+            need_mask |= !(wk_lo == wk_hi && qdl == qdh && qdl == wk_lo);
+        }
         if (skip) return;
         // per-lane rows of block rb of the accumulator: i0 + 32*rb + 8*a + 4*hi + (0..3),
         // their lse2 and D from the copy in LDS (pad rows hold no data and are masked)
@@ -482,6 +522,8 @@ void bwd_dkdv_kernel(BwdParams p) {
                             bool keep = key_ok && i < p.Sq;
                             if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
                             if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
+                            if ((MASK & MASK_DOC) && pred)
+                                keep &= p.qdoc[b * p.qdoc_sb + min(i, p.Sq - 1)] == mykdoc;
                             x = keep ? fast_exp2(t - lse2) : 0.f;
                             ds[u] = keep ? x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]) : 0.f;
                         } else {
@@ -568,12 +610,14 @@ hipError_t launch_bwd_one(BwdParams p, hipStream_t s) {
 
 template <typename TT, int D>
 hipError_t launch_bwd_t(const BwdParams &p, bool alibi, int mask, hipStream_t s) {
-#define MM_CASE(A, M) case (A) * 8 + (M): return launch_bwd_one<TT, D, (A) != 0, (M)>(p, s);
-    switch ((alibi ? 8 : 0) + (mask & 7)) {
+#define MM_CASE(A, M) case (A) * 16 + (M): return launch_bwd_one<TT, D, (A) != 0, (M)>(p, s);
+    switch ((alibi ? 16 : 0) + (mask & 15)) {
         MM_CASE(0, 0) MM_CASE(0, 1) MM_CASE(0, 2) MM_CASE(0, 3)
         MM_CASE(0, 4) MM_CASE(0, 5) MM_CASE(0, 6) MM_CASE(0, 7)
+        MM_CASE(0, 8) MM_CASE(0, 9) MM_CASE(0, 12) MM_CASE(0, 13)
         MM_CASE(1, 0) MM_CASE(1, 1) MM_CASE(1, 2) MM_CASE(1, 3)
         MM_CASE(1, 4) MM_CASE(1, 5) MM_CASE(1, 6) MM_CASE(1, 7)
+        MM_CASE(1, 8) MM_CASE(1, 9) MM_CASE(1, 12) MM_CASE(1, 13)
         default: return hipErrorInvalidValue;
     }
 #undef MM_CASE

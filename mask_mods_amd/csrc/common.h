@@ -89,4 +89,25 @@ __device__ __forceinline__ int xcd_remap(int p, int n) {
     return x * q + (x < r ? x : r) + s;
 }
 
+// On a non-decreasing int32 array of n entries: the first index whose value is >= v
+// (lower) or > v (upper); n if none.
+__device__ __forceinline__ int doc_lower(const int32_t *a, int n, int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < v) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+__device__ __forceinline__ int doc_upper(const int32_t *a, int n, int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] <= v) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
 }  // namespace mm

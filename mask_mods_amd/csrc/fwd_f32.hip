@@ -41,6 +41,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p, int alibi, int
         j_lo = max(j_lo, row - p.window);
         j_hi = min(j_hi, row + p.window + 1);
     }
+    const int32_t *kd = (mask & MASK_DOC) ? p.kvdoc + b * p.kvdoc_sb : nullptr;
+    const int mydoc = kd ? p.qdoc[b * p.qdoc_sb + row] : 0;
+    if (kd && !bm_row) {
+        j_lo = max(j_lo, doc_lower(kd, p.Skv, mydoc));
+        j_hi = min(j_hi, doc_upper(kd, p.Skv, mydoc));
+    }
     bool dropped = false;
     if (p.rowdrop) dropped = fmix32(p.rd_seed ^ (uint32_t)rid) < p.rd_thr;
     if (dropped) j_hi = j_lo;
@@ -52,6 +58,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p, int alibi, int
             if (blk == 0) continue;
             if (blk == 1 && (mask & MASK_CAUSAL) && j > row) continue;
             if (blk == 1 && (mask & MASK_WINDOW) && abs(row - j) > p.window) continue;
+            if (blk == 1 && kd && kd[j] != mydoc) continue;
         }
         const float *kr = kg + (int64_t)j * p.k_ss;
         float t = 0.f;

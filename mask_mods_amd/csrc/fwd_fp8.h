@@ -119,6 +119,22 @@ void fwd_fp8_kernel(FwdParams p) {
         j_lo = max(0, q0 - p.window);
         if (!(MASK & MASK_CAUSAL)) j_hi = min(j_hi, row_max + p.window + 1);
     }
+    if (MASK & MASK_DOC) {
+        // packed documents: only keys whose document lies within the tile's rows' range
+        const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
+        if (!(MASK & MASK_BLOCK)) {
+            j_lo = max(j_lo, doc_lower(kd, p.Skv, qd[q0]));
+            j_hi = min(j_hi, doc_upper(kd, p.Skv, qd[row_max]));
+        }
+    }
+    // document ids of the wave's first and last rows and of the lane's row
+    int wd_lo = 0, wd_hi = 0, mydoc = 0;
+    if (MASK & MASK_DOC) {
+        const int32_t *qd = p.qdoc + b * p.qdoc_sb;
+        wd_lo = qd[min(r0, p.Sq - 1)];
+        wd_hi = qd[min(r0 + 31, p.Sq - 1)];
+        mydoc = qd[min(row, p.Sq - 1)];
+    }
     const int kt_lo = j_lo / BN;
     const int kt_hi = j_hi > j_lo ? (j_hi + BN - 1) / BN : kt_lo;
 
@@ -220,6 +236,12 @@ void fwd_fp8_kernel(FwdParams p) {
             dead |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
+        if ((MASK & MASK_DOC) && pred) {
+            const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
+            const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
+            dead |= kdh < wd_lo || kdl > wd_hi;
+            need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
+        }
         if (!(ALIBI || need_mask || !(c2 > 0.f))) return c2;
         const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
         auto scores = [&](bool masked) {
@@ -234,6 +256,8 @@ void fwd_fp8_kernel(FwdParams p) {
                         bool keep = (j < p.Skv) & !dead;
                         if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
                         if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                        if ((MASK & MASK_DOC) && pred)
+                            keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
                         t = keep ? t : -INFINITY;
                     }
                     sacc[kb][e] = t;
@@ -424,12 +448,14 @@ hipError_t launch_fwd_fp8_one(FwdParams p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_fwd_fp8(const FwdParams &p, bool alibi, int mask, hipStream_t s) {
-#define MM_CASE(A, M) case (A) * 8 + (M): return launch_fwd_fp8_one<D, (A) != 0, (M)>(p, s);
-    switch ((alibi ? 8 : 0) + (mask & 7)) {
+#define MM_CASE(A, M) case (A) * 16 + (M): return launch_fwd_fp8_one<D, (A) != 0, (M)>(p, s);
+    switch ((alibi ? 16 : 0) + (mask & 15)) {
         MM_CASE(0, 0) MM_CASE(0, 1) MM_CASE(0, 2) MM_CASE(0, 3)
         MM_CASE(0, 4) MM_CASE(0, 5) MM_CASE(0, 6) MM_CASE(0, 7)
+        MM_CASE(0, 8) MM_CASE(0, 9) MM_CASE(0, 12) MM_CASE(0, 13)
         MM_CASE(1, 0) MM_CASE(1, 1) MM_CASE(1, 2) MM_CASE(1, 3)
         MM_CASE(1, 4) MM_CASE(1, 5) MM_CASE(1, 6) MM_CASE(1, 7)
+        MM_CASE(1, 8) MM_CASE(1, 9) MM_CASE(1, 12) MM_CASE(1, 13)
         default: return hipErrorInvalidValue;
     }
 #undef MM_CASE

@@ -25,7 +25,7 @@
 // Softmax: scores are kept in base-2 units (t = scale*log2(e)*q.k [+ slope*log2(e)*(j-i)]).
 // The running max is only raised when a tile's max exceeds it by more than 2^8 in
 // probability (lazy rescale): P then stays <= 256, exact in the final O / l. Row sums
-// are accumulated from the same 16-bit P values that feed the PV product (v_dot2).
+// add the fp32 P values; the PV product takes them rounded to 16 bits.
 // Semantics (FlyDSL PR #931, Summary): score_mod sees the scaled score, the mask_mod is
 // applied after it, and rows with no kept key give O = 0, LSE = -inf (the running max
 // is clamped to 0 while it is -inf, and the epilogue guards 1/l).
@@ -39,15 +39,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// row sum helper: acc + p.x + p.y on the 16-bit pair that feeds the PV MFMA
-__device__ __forceinline__ float dot2_ones(uint32_t pair, float acc, BF16) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
-}
-__device__ __forceinline__ float dot2_ones(uint32_t pair, float acc, F16) {
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), ones, acc, false);
-}
 __device__ __forceinline__ uint32_t pack2(float a, float b, BF16) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
@@ -142,6 +133,22 @@ void fwd_mfma_kernel(FwdParams p) {
         j_lo = max(0, q0 - p.window);
         if (!(MASK & MASK_CAUSAL)) j_hi = min(j_hi, row_max + p.window + 1);
     }
+    if (MASK & MASK_DOC) {
+        // packed documents: only keys whose document lies within the tile's rows' range
+        const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
+        if (!(MASK & MASK_BLOCK)) {
+            j_lo = max(j_lo, doc_lower(kd, p.Skv, qd[q0]));
+            j_hi = min(j_hi, doc_upper(kd, p.Skv, qd[row_max]));
+        }
+    }
+    // document ids of the wave's first and last rows and of the lane's row
+    int wd_lo = 0, wd_hi = 0, mydoc = 0;
+    if (MASK & MASK_DOC) {
+        const int32_t *qd = p.qdoc + b * p.qdoc_sb;
+        wd_lo = qd[min(r0, p.Sq - 1)];
+        wd_hi = qd[min(r0 + 31, p.Sq - 1)];
+        mydoc = qd[min(row, p.Sq - 1)];
+    }
     const int kt_lo = j_lo / BN;
     const int kt_hi = j_hi > j_lo ? (j_hi + BN - 1) / BN : kt_lo;
 
@@ -233,6 +240,12 @@ void fwd_mfma_kernel(FwdParams p) {
             skip |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
+        if ((MASK & MASK_DOC) && pred && !skip) {
+            const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
+            const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
+            skip |= kdh < wd_lo || kdl > wd_hi;
+            need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
+        }
 
         if (!skip) {
             f32x16 sacc[NKB];
@@ -273,6 +286,8 @@ void fwd_mfma_kernel(FwdParams p) {
                             bool keep = j < p.Skv;
                             if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
                             if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                            if ((MASK & MASK_DOC) && pred)
+                                keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
                             t = keep ? t : -INFINITY;
                         }
                         sacc[kb][e] = t;
@@ -299,9 +314,11 @@ void fwd_mfma_kernel(FwdParams p) {
                 m_run = m_new;
             }
             const float nm = m_run == -INFINITY ? 0.f : -m_run;
-            // P = 2^(t - m) as 16-bit pairs; row sum from the same 16-bit values
+            // P = 2^(t - m) as 16-bit pairs for the PV product; the row sum adds the fp32
+            // values (a sum of the 16-bit roundings would put up to 2^-9 of relative
+            // error into the LSE of rows with few keys)
             uint32_t pp[NKB][8];
-            float psum = 0.f;
+            float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -309,9 +326,10 @@ void fwd_mfma_kernel(FwdParams p) {
                     const float x0 = fast_exp2(fmaf(sacc[kb][2 * e2], cc, nm));
                     const float x1 = fast_exp2(fmaf(sacc[kb][2 * e2 + 1], cc, nm));
                     pp[kb][e2] = pack2(x0, x1, TT{});
-                    psum = dot2_ones(pp[kb][e2], psum, TT{});
+                    psum0 += x0;
+                    psum1 += x1;
                 }
-            l_run += psum;
+            l_run += psum0 + psum1;
             // O^T += V^T P^T (all transposed V reads first, then the MFMAs)
             {
                 u32x4 va[BN / 16][DB];
@@ -441,13 +459,15 @@ hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
 
 template <typename TT, int D>
 hipError_t launch_fwd_mfma(const FwdParams &p, bool alibi, int mask, hipStream_t s) {
-#define MM_CASE(A, M) case (A) * 8 + (M): return launch_fwd_mfma_one<TT, D, (A) != 0, (M)>(p, s);
-    switch ((alibi ? 8 : 0) + (mask & 7)) {
+#define MM_CASE(A, M) case (A) * 16 + (M): return launch_fwd_mfma_one<TT, D, (A) != 0, (M)>(p, s);
+    switch ((alibi ? 16 : 0) + (mask & 15)) {
         MM_CASE(0, 0) MM_CASE(0, 1) MM_CASE(0, 2) MM_CASE(0, 3)
         MM_CASE(0, 4) MM_CASE(0, 5) MM_CASE(0, 6) MM_CASE(0, 7)
+        MM_CASE(0, 8) MM_CASE(0, 9) MM_CASE(0, 12) MM_CASE(0, 13)
         MM_CASE(1, 0) MM_CASE(1, 1) MM_CASE(1, 2) MM_CASE(1, 3)
         MM_CASE(1, 4) MM_CASE(1, 5) MM_CASE(1, 6) MM_CASE(1, 7)
-        default: return hipErrorInvalidValue;
+        MM_CASE(1, 8) MM_CASE(1, 9) MM_CASE(1, 12) MM_CASE(1, 13)
+        default: return hipErrorInvalidValue;  // document mask with a window: not built
     }
 #undef MM_CASE
 }

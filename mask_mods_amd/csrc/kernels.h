@@ -7,7 +7,7 @@
 
 namespace mm {
 
-enum { MASK_CAUSAL = 1, MASK_WINDOW = 2, MASK_BLOCK = 4 };
+enum { MASK_CAUSAL = 1, MASK_WINDOW = 2, MASK_BLOCK = 4, MASK_DOC = 8 };
 
 // block-mask granularity: query rows x keys per block
 constexpr int kBlockQ = 128, kBlockKV = 64;
@@ -31,6 +31,8 @@ struct FwdParams {
     const uint8_t *bm;     // block mask or nullptr: byte b*bm_sb + h*bm_sh + qblk*bm_sq + kblk
     int64_t bm_sb, bm_sh, bm_sq;
     float v_descale;       // fp8 inputs: V dequantisation factor (the Q/K ones are in scale_log2)
+    const int32_t *qdoc, *kvdoc;  // document ids (non-decreasing per sequence) or nullptr
+    int64_t qdoc_sb, kvdoc_sb;
 };
 
 // Backward (dQ, dK, dV). Strides are in elements.
@@ -50,6 +52,8 @@ struct BwdParams {
     const uint8_t *bm;     // block mask or nullptr (as FwdParams)
     int64_t bm_sb, bm_sh, bm_sq;
     int n_tiles;           // q tiles (dQ kernel) or key tiles (dK/dV kernel) per head
+    const int32_t *qdoc, *kvdoc;  // document ids (non-decreasing per sequence) or nullptr
+    int64_t qdoc_sb, kvdoc_sb;
 };
 
 // Decode split pass + merge. Strides are in elements.

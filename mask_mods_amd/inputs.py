@@ -193,3 +193,27 @@ def random_block_mask(seed: int, shape, p_empty: float = 0.4, p_full: float = 0.
     """
     u = rng(seed).random(shape)
     return np.where(u < p_empty, 0, np.where(u < p_empty + p_full, 2, 1)).astype(np.uint8)
+
+
+def packed_document_ids(seed: int, B: int, S: int, n_docs: int, first_id: int = 0) -> np.ndarray:
+    """int32 [B, S] document ids of sequences packed back to back: per batch row,
+    n_docs documents (at most S) whose lengths come from n_docs - 1 distinct cut points
+    drawn uniformly, so the lengths are mixed (single-token documents included as the
+    draw falls) and the ids run first_id, first_id + 1, ... without decreasing.
+    """
+    g = rng(seed)
+    out = np.empty((B, S), dtype=np.int32)
+    n = max(1, min(n_docs, S))
+    for b in range(B):
+        cuts = np.sort(g.choice(np.arange(1, S), size=n - 1, replace=False)) if n > 1 else np.array([], int)
+        ids = np.zeros(S, dtype=np.int32)
+        ids[cuts] = 1
+        out[b] = first_id + np.cumsum(ids)
+    return out
+
+
+def document_ids_from_lengths(lengths, S: int | None = None) -> np.ndarray:
+    """int32 [S] ids 0, 0, .., 1, .. for documents of the given lengths, in order."""
+    ids = np.repeat(np.arange(len(lengths), dtype=np.int32), np.asarray(lengths, dtype=np.int64))
+    assert S is None or ids.size == S
+    return ids

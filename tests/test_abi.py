@@ -34,7 +34,8 @@ def test_struct_layouts_match():
     lib = mm.load_library()
     assert lib.mm_fwd_args_size() == ctypes.sizeof(mm.FwdArgs)
     assert lib.mm_decode_args_size() == ctypes.sizeof(mm.DecodeArgs)
-    assert lib.mm_version() >= 200
+    assert lib.mm_bwd_args_size() == ctypes.sizeof(mm.BwdArgs)
+    assert lib.mm_version() >= 400
 
 
 def test_status_strings():
@@ -76,7 +77,7 @@ def _fwd(**kw):
     (dict(D=96), UNSUP),
     (dict(D=256), UNSUP),
     (dict(mods_score_mod=9), UNSUP),
-    (dict(mods_mask_flags=8), UNSUP),
+    (dict(mods_mask_flags=16), UNSUP),
     (dict(mods_mask_flags=2, mods_window=-1), SHAPE),
     (dict(q_strides=mm._I64x3(-1, 0, 0)), STRIDE),
     (dict(k_strides=mm._I64x3(100, 12, 128)), STRIDE),
@@ -192,3 +193,67 @@ def test_decode_rejects_bad_page_tables(page_size, stride, status):
     # B = 2 with Scap = 128: 8 pages of 16 per sequence
     assert _dec(B=2, Scap=128, kv_len=100, block_table=FAKE, page_size=page_size,
                 block_table_stride=stride) == status
+
+
+DOC = dict(mods_mask_flags=8, mods_q_doc_ids=FAKE, mods_kv_doc_ids=FAKE + 64)
+BAD_Q_STRIDE = dict(q_strides=mm._I64x3(-1, 0, 0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mods_mask_flags=8), NULL),                               # ids missing
+    (dict(DOC, mods_kv_doc_ids=None), NULL),
+    (dict(DOC, mods_mask_flags=8 | 2, mods_window=4), UNSUP),      # not with the window
+    (dict(DOC, mods_doc_strides=mm._I64x2(0, -16)), STRIDE),
+    (dict(DOC, mods_q_doc_ids=FAKE + 2), STRIDE),                  # int32 alignment
+    (dict(DOC, **BAD_Q_STRIDE), STRIDE),                           # ids accepted: reaches the stride check
+    (dict(DOC, mods_mask_flags=8 | 1 | 4, **BAD_Q_STRIDE), STRIDE),
+    (dict(mods_mask_flags=8, Sq=0), OK),                           # no pair: ids not needed
+])
+def test_document_mask_args_rejected_before_launch(kw, status):
+    assert _fwd(**kw) == status
+
+
+def _bwd(**kw):
+    a = mm.BwdArgs()
+    a.q = a.k = a.v = a.out = a.dout = a.lse = a.dq = a.dk = a.dv = FAKE
+    a.dtype = 2
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = 1, 4, 2, 16, 16, 128
+    for name, h in (("q", 4), ("k", 2), ("v", 2), ("o", 4), ("do", 4), ("dq", 4), ("dk", 2), ("dv", 2)):
+        setattr(a, name + "_strides", mm._I64x3(h * 16 * 128, 16 * 128, 128))
+    a.scale = 0.1
+    a.workspace = FAKE
+    a.workspace_bytes = 1 << 20
+    for key, val in kw.items():
+        if key.startswith("mods_"):
+            setattr(a.mods, key[5:], val)
+        else:
+            setattr(a, key, val)
+    return mm.load_library().mm_attn_bwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), NULL),
+    (dict(dk=None), NULL),
+    (dict(dtype=0), DTYPE),                      # the backward is 16-bit only
+    (dict(dtype=3), DTYPE),
+    (dict(Hq=3), SHAPE),
+    (dict(D=32), UNSUP),
+    (dict(mods_mask_flags=16), UNSUP),
+    (dict(do_strides=mm._I64x3(0, 0, 12)), STRIDE),
+    (dict(dv=FAKE + 4), STRIDE),
+    (dict(workspace=None), WORKSPACE),
+    (dict(workspace_bytes=8), WORKSPACE),
+    (dict(mods_mask_flags=8), NULL),
+    (dict(DOC, mods_mask_flags=8 | 2), UNSUP),
+    (dict(DOC, mods_doc_strides=mm._I64x2(-1, 0)), STRIDE),
+    (dict(DOC, do_strides=mm._I64x3(0, 0, 12)), STRIDE),
+    (dict(B=0), OK),
+])
+def test_bwd_rejects_before_launch(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    # lse2 and D per row, rows padded to 64 per (b, h)
+    assert mm.bwd_workspace_size(2, 3, 100) == 2 * 2 * 3 * 128 * 4
+    assert mm.bwd_workspace_size(1, 1, 0) == 0

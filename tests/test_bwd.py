@@ -19,12 +19,13 @@ RD = (20240, int(0.05 * 2 ** 32))
 
 
 def _grads(B, Hq, Hkv, Sq, Skv, D, dtype, *, causal=False, window=None, alibi=False,
-           rowdrop=False, block_mask=None, seed=0, scale=None):
+           rowdrop=False, block_mask=None, q_doc=None, kv_doc=None, seed=0, scale=None):
     """Run forward + backward on the GPU; return device grads and the f64 inputs."""
     import torch
     import mask_mods_amd as mm
     print(f"[bwd] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal} "
-          f"window={window} alibi={alibi} rowdrop={rowdrop} block={block_mask is not None} seed={seed}",
+          f"window={window} alibi={alibi} rowdrop={rowdrop} block={block_mask is not None} "
+          f"docs={None if q_doc is None else int(q_doc.max()) + 1} seed={seed}",
           flush=True)
     x = inputs.attention_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
     g = inputs.rng(seed + 1000)
@@ -34,7 +35,8 @@ def _grads(B, Hq, Hkv, Sq, Skv, D, dtype, *, causal=False, window=None, alibi=Fa
         scale = float(np.float32(1.0 / math.sqrt(D)))
     kw = dict(causal=causal, window=window, score_mod=mm.SCORE_ALIBI if alibi else mm.SCORE_NONE,
               rowdrop=RD if rowdrop else None,
-              block_mask=torch.from_numpy(block_mask).cuda() if block_mask is not None else None)
+              block_mask=torch.from_numpy(block_mask).cuda() if block_mask is not None else None,
+              q_doc=_ids(q_doc), kv_doc=_ids(kv_doc))
     out, lse = mm.attn_fwd(q, k, v, scale, **kw)
     dq, dk, dv = mm.attn_bwd(q, k, v, out, lse, do, scale, **kw)
     torch.cuda.synchronize()
@@ -42,12 +44,18 @@ def _grads(B, Hq, Hkv, Sq, Skv, D, dtype, *, causal=False, window=None, alibi=Fa
     return (dq, dk, dv), f64, scale
 
 
+def _ids(ids):
+    import torch
+    return None if ids is None else torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+
+
 def _check(B, Hq, Hkv, Sq, Skv, D, dtype, **mods):
     (dq, dk, dv), (qd, kd, vd, dod), scale = _grads(B, Hq, Hkv, Sq, Skv, D, dtype, **mods)
     ref = oracle.attention_bwd(qd, kd, vd, dod, scale=scale, causal=mods.get("causal", False),
                                window=mods.get("window"), alibi=mods.get("alibi", False),
                                rowdrop=RD if mods.get("rowdrop") else None,
-                               block_mask=mods.get("block_mask"))
+                               block_mask=mods.get("block_mask"), q_doc=mods.get("q_doc"),
+                               kv_doc=mods.get("kv_doc"))
     for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         err = assert_parity(to_f64(got), want, O_ATOL, O_RTOL, name)
         print(f"[bwd] {name} max|err| {err:.3e} max|ref| {np.abs(want).max():.3e}", flush=True)
@@ -142,5 +150,56 @@ def test_config_2048_sampled_heads(causal):
     for b, h in ((0, 0), (1, 31)):
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = oracle.attention_bwd(qd[sl], kd[sl], vd[sl], dod[sl], scale=scale, causal=causal)
+        for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            assert_parity(to_f64(got[sl]), want, O_ATOL, O_RTOL, f"{name}[{b},{h}]")
+
+
+# ------------------------------------------------------------ document mask
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_document_mask(dtype, D, causal):
+    docs = inputs.packed_document_ids(30, 2, 300, 5)
+    _check(2, 4, 2, 300, 300, D, dtype, seed=30, causal=causal, q_doc=docs)
+
+
+def test_document_mask_tile_aligned_and_single_token_documents():
+    docs = inputs.document_ids_from_lengths([64, 1, 63, 128, 1, 200, 55], 512)[None]
+    _check(1, 4, 4, 512, 512, 128, "bf16", seed=31, causal=True, alibi=True, q_doc=docs)
+
+
+def test_document_mask_cross_attention_with_a_document_without_keys():
+    """Query document 2 has no keys and key document 4 no queries: zero gradients there."""
+    qd = inputs.document_ids_from_lengths([90, 70, 40, 100], 300)[None]
+    kd = np.concatenate([inputs.document_ids_from_lengths([200, 150], 350),
+                         np.full(300, 3, np.int32), np.full(50, 4, np.int32)])[None]
+    dq, dk, dv = _check(1, 4, 2, 300, 700, 128, "bf16", seed=32, q_doc=qd, kv_doc=kd)
+    assert np.all(to_f64(dq)[:, :, 160:200] == 0)
+    # key document 4 has no query rows
+    assert np.all(to_f64(dk)[:, :, 650:] == 0) and np.all(to_f64(dv)[:, :, 650:] == 0)
+
+
+def test_document_mask_with_block_mask():
+    S = 384
+    bm = inputs.random_block_mask(33, (1, 4, -(-S // 128), -(-S // 64)))
+    docs = inputs.packed_document_ids(33, 1, S, 4)
+    _check(1, 4, 2, S, S, 128, "bf16", seed=33, causal=True, block_mask=bm, q_doc=docs)
+
+
+def test_document_mask_rowdrop_gqa():
+    docs = inputs.packed_document_ids(34, 2, 257, 3)
+    _check(2, 8, 2, 257, 257, 64, "f16", seed=34, causal=True, rowdrop=True, q_doc=docs)
+
+
+def test_document_mask_2048_sampled_heads():
+    """B2 H16 D128 S2048 causal with 12 packed documents; two heads recomputed in full."""
+    B, H, S, D = 2, 16, 2048, 128
+    docs = inputs.packed_document_ids(35, B, S, 12)
+    (dq, dk, dv), (qd, kd, vd, dod), scale = _grads(B, H, H, S, S, D, "bf16", seed=35, causal=True,
+                                                    q_doc=docs)
+    for b, h in ((0, 3), (1, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_bwd(qd[sl], kd[sl], vd[sl], dod[sl], scale=scale, causal=True,
+                                   q_doc=docs[b:b + 1])
         for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
             assert_parity(to_f64(got[sl]), want, O_ATOL, O_RTOL, f"{name}[{b},{h}]")

@@ -53,19 +53,21 @@ def _integer_inputs(seed, B, Hq, Hkv, Sq, Skv, D):
 
 
 def _run(x, D, *, scale, exact, causal=False, window=None, alibi=False, rowdrop=False,
-         block_mask=None, rows=None, label=""):
+         block_mask=None, q_doc=None, rows=None, label=""):
     import torch
     import mask_mods_amd as mm
     B, Hq, Sq, _ = x["q"].shape
     Skv = x["k"].shape[2]
     print(f"[fp8] {label} shape={x['q'].shape}/{x['k'].shape} exact={exact} causal={causal} "
-          f"window={window} alibi={alibi} rowdrop={rowdrop} block={block_mask is not None}", flush=True)
+          f"window={window} alibi={alibi} rowdrop={rowdrop} block={block_mask is not None} "
+          f"docs={q_doc is not None}", flush=True)
     dq, dk, dv = x["descale_q"], x["descale_k"], x["descale_v"]
     q, k, v = _dev8(x["q"]), _dev8(x["k"]), _dev8(x["v"])
     bm = torch.from_numpy(block_mask).cuda() if block_mask is not None else None
     out, lse = mm.attn_fwd(q, k, v, scale, causal=causal, window=window,
                            score_mod=mm.SCORE_ALIBI if alibi else mm.SCORE_NONE,
-                           rowdrop=RD if rowdrop else None, block_mask=bm, descale=(dq, dk, dv))
+                           rowdrop=RD if rowdrop else None, block_mask=bm, descale=(dq, dk, dv),
+                           q_doc=None if q_doc is None else torch.from_numpy(q_doc).cuda())
     torch.cuda.synchronize()
     assert out.dtype == torch.bfloat16
     qd = inputs.e4m3_bits_to_f64(x["q"]) * dq
@@ -73,7 +75,7 @@ def _run(x, D, *, scale, exact, causal=False, window=None, alibi=False, rowdrop=
     vd = inputs.e4m3_bits_to_f64(x["v"]) * dv
     O, L, wsq, wvar = oracle.attention(qd, kd, vd, scale=scale, causal=causal, window=window,
                                        alibi=alibi, rowdrop=RD if rowdrop else None,
-                                       block_mask=block_mask, rows=rows, sensitivity=True)
+                                       block_mask=block_mask, q_doc=q_doc, rows=rows, sensitivity=True)
     got_o, got_l = to_f64(out), to_f64(lse)
     if rows is not None:
         got_o, got_l = got_o.reshape(-1, D)[rows], got_l.reshape(-1)[rows]
@@ -174,3 +176,26 @@ def test_config_8192_sampled(causal):
     rows = inputs.sample_rows(8, B, H, S, n_random=64)
     _run(x, D, scale=float(np.float32(1 / math.sqrt(D))), exact=False, causal=causal, rows=rows,
          label="8192")
+
+
+@pytest.mark.parametrize("case", ["none", "causal", "rowdrop_causal"])
+def test_integer_scores_document_mask(case):
+    x = _integer_inputs(9, 2, 4, 2, 700, 700, 128)
+    docs = inputs.packed_document_ids(9, 2, 700, 6)
+    _run(x, 128, scale=LN2, exact=True, q_doc=docs, label="doc " + case, **EXACT_CASES[case])
+
+
+def test_integer_scores_document_mask_with_block_mask():
+    S = 700
+    x = _integer_inputs(10, 1, 4, 4, S, S, 64)
+    bm = inputs.random_block_mask(10, (1, 4, -(-S // 128), -(-S // 64)))
+    docs = inputs.packed_document_ids(10, 1, S, 5)
+    _run(x, 64, scale=LN2, exact=True, causal=True, block_mask=bm, q_doc=docs, label="doc block")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_random_document_mask_within_derived_bound(D):
+    x = inputs.attention_inputs_fp8(11, 2, 4, 4, 1024, 1024, D)
+    docs = inputs.packed_document_ids(11, 2, 1024, 7)
+    _run(x, D, scale=float(np.float32(1 / math.sqrt(D))), exact=False, causal=True, alibi=True,
+         q_doc=docs, label="doc")
