@@ -63,6 +63,10 @@ struct Tile {
     __host__ __device__ static constexpr int off(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
 };
 
+#ifndef MM_FWD_NW
+#define MM_FWD_NW 8  // waves per workgroup without a mask mod
+#endif
+
 template <typename TT, int D, bool ALIBI, int MASK, int NW, int NST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
@@ -222,16 +226,16 @@ void fwd_mfma_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // one tile: DMA tile `next` (if >= 0) into (Kn, Vn) while computing tile kt on
-    // (Kt, Vt). `blk` is the tile's block-mask class: 1 = the mask_mod predicates
-    // decide, 2 = every pair kept (predicates not evaluated).
-    auto tile = [&](int kt, int blk, const unsigned char *Kt, const unsigned char *Vt, int next,
-                    unsigned char *Kn, unsigned char *Vn) {
-        if (next >= 0) load_tile(next, Kn, Vn);
+    // ---- the pieces of one tile ----
+    // Whether this wave skips tile kt, and whether the tile needs per-pair masking.
+    // `blk` is the tile's block-mask class: 1 = the mask_mod predicates decide,
+    // 2 = every pair kept (predicates not evaluated).
+    auto classify = [&](int kt, int blk, bool &need_mask) -> bool {
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
         const bool pred = blk == 1;  // predicates apply in this tile
-        bool skip = kt >= kt_hi, need_mask = k0 + BN > p.Skv;
+        bool skip = kt >= kt_hi;
+        need_mask = k0 + BN > p.Skv;
         if ((MASK & MASK_CAUSAL) && pred) {
             skip |= k0 > r_last;
             need_mask |= k0 + BN - 1 > r0;
@@ -246,114 +250,176 @@ void fwd_mfma_kernel(FwdParams p) {
             skip |= kdh < wd_lo || kdl > wd_hi;
             need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
         }
-
-        if (!skip) {
-            f32x16 sacc[NKB];
-            {
-                // all K fragments first, then the MFMAs: the reads overlap each other
-                // instead of each MFMA waiting on its own read
-                u32x4 ka[NKB][KS];
+        return skip;
+    };
+    // S^T = K Q^T for the tile in Kt
+    auto qk = [&](const unsigned char *Kt, f32x16 (&sacc)[NKB]) {
+        if (MASK & MASK_BLOCK) {
+            // the block walk holds a few more registers: fragments of one 32-key block
+            // at a time keep the loop within 256 VGPRs
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
+            for (int kb = 0; kb < NKB; ++kb) {
+                u32x4 ka[KS];
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        ka[kb][ks] = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[ks]);
+                for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[ks]);
+                sacc[kb] = f32x16{};
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    sacc[kb] = f32x16{};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) sacc[kb] = mfma32x32x16(as_vec<V8>(ka[kb][ks]), qf[ks], sacc[kb]);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, NKB * KS, 0);  // DS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, NKB * KS, 0);  // then MFMAs
+                for (int ks = 0; ks < KS; ++ks) sacc[kb] = mfma32x32x16(as_vec<V8>(ka[ks]), qf[ks], sacc[kb]);
             }
-            // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4.
-            // general tiles (alibi, masking, non-positive scale) store t in sacc and use
-            // cc = 1; plain tiles keep the raw dot products and fold the scale into the
-            // exponent (cc = scale*log2e > 0 commutes with the max).
-            float mloc = -INFINITY, cc;
-            const bool general = ALIBI || need_mask || !(c2 > 0.f);
-            if (general) {
-                const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
+                __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // DS reads of block kb
+                __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);  // its MFMAs
+            }
+            return;
+        }
+        // all K fragments first, then the MFMAs: the reads overlap each other instead of
+        // each MFMA waiting on its own read
+        u32x4 ka[NKB][KS];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
-                        float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
-                        if (need_mask) {
-                            const int j = k0 + 4 * hi + jo;
-                            bool keep = j < p.Skv;
-                            if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
-                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                            if ((MASK & MASK_DOC) && pred)
-                                keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
-                            t = keep ? t : -INFINITY;
-                        }
-                        sacc[kb][e] = t;
-                        mloc = fmaxf(mloc, t);
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ka[kb][ks] = *(const u32x4 *)(Kt + kb * 32 * TL::ROWB + koff[ks]);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            sacc[kb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sacc[kb] = mfma32x32x16(as_vec<V8>(ka[kb][ks]), qf[ks], sacc[kb]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, NKB * KS, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, NKB * KS, 0);  // then MFMAs
+    };
+    // scale, score_mod and mask_mod, the running max (lazily rescaling O and l), then
+    // P = 2^(t - m) as 16-bit pairs and the row sum
+    auto softmax = [&](int kt, int blk, bool need_mask, f32x16 (&sacc)[NKB], uint32_t (&pp)[NKB][8]) {
+        const int k0 = kt * BN;
+        const bool pred = blk == 1;
+        // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4.
+        // general tiles (alibi, masking, non-positive scale) store t in sacc and use
+        // cc = 1; plain tiles keep the raw dot products and fold the scale into the
+        // exponent (cc = scale*log2e > 0 commutes with the max).
+        float mloc = -INFINITY, cc;
+        const bool general = ALIBI || need_mask || !(c2 > 0.f);
+        if (general) {
+            const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
+                    float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
+                    if (need_mask) {
+                        const int j = k0 + 4 * hi + jo;
+                        bool keep = j < p.Skv;
+                        if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
+                        if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                        if ((MASK & MASK_DOC) && pred)
+                            keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
+                        t = keep ? t : -INFINITY;
                     }
+                    sacc[kb][e] = t;
+                    mloc = fmaxf(mloc, t);
                 }
-                cc = 1.f;
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
-                mloc *= c2;
-                cc = c2;
             }
-            mloc = row_max2(mloc);
-            // lazy rescale: raise the running max only when the tile exceeds it by > 2^8
-            if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescale)) {
-                const float m_new = fmaxf(m_run, mloc);
-                const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-                m_run = m_new;
-            }
-            const float nm = m_run == -INFINITY ? 0.f : -m_run;
-            // P = 2^(t - m) as 16-bit pairs for the PV product; the row sum adds the fp32
-            // values (a sum of the 16-bit roundings would put up to 2^-9 of relative
-            // error into the LSE of rows with few keys)
-            uint32_t pp[NKB][8];
-            float psum0 = 0.f, psum1 = 0.f;
+            cc = 1.f;
+        } else {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int e2 = 0; e2 < 8; ++e2) {
-                    const float x0 = fast_exp2(fmaf(sacc[kb][2 * e2], cc, nm));
-                    const float x1 = fast_exp2(fmaf(sacc[kb][2 * e2 + 1], cc, nm));
-                    pp[kb][e2] = pack2(x0, x1, TT{});
-                    psum0 += x0;
-                    psum1 += x1;
-                }
-            l_run += psum0 + psum1;
-            // O^T += V^T P^T (all transposed V reads first, then the MFMAs)
-            {
-                u32x4 va[BN / 16][DB];
+                for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
+            mloc *= c2;
+            cc = c2;
+        }
+        mloc = row_max2(mloc);
+        // lazy rescale: raise the running max only when the tile exceeds it by > 2^8
+        if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescale)) {
+            const float m_new = fmaxf(m_run, mloc);
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            l_run *= alpha;
 #pragma unroll
-                for (int ks = 0; ks < BN / 16; ++ks)
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float nm = m_run == -INFINITY ? 0.f : -m_run;
+        // P = 2^(t - m) as 16-bit pairs for the PV product; the row sum adds the fp32
+        // values (a sum of the 16-bit roundings would put up to 2^-9 of relative
+        // error into the LSE of rows with few keys)
+        float psum = 0.f;
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][0]));
-                        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][1]));
-                        const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi4);
-                        va[ks][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-                    }
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int ks = 0; ks < BN / 16; ++ks) {
-                    const int kb = ks >> 1, o4 = 4 * (ks & 1);
-                    const V8 pf = as_vec<V8>(u32x4{pp[kb][o4], pp[kb][o4 + 1], pp[kb][o4 + 2], pp[kb][o4 + 3]});
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(as_vec<V8>(va[ks][db]), pf, oacc[db]);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (BN / 16) * DB, 1);
-                __builtin_amdgcn_sched_group_barrier(0x008, (BN / 16) * DB, 1);
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const float x0 = fast_exp2(fmaf(sacc[kb][2 * e2], cc, nm));
+                const float x1 = fast_exp2(fmaf(sacc[kb][2 * e2 + 1], cc, nm));
+                pp[kb][e2] = pack2(x0, x1, TT{});
+                psum += x0;
+                psum += x1;
             }
+        l_run += psum;
+    };
+    // O^T += V^T P^T for the tile in Vt (all transposed V reads first, then the MFMAs)
+    auto pv = [&](const unsigned char *Vt, const uint32_t (&pp)[NKB][8]) {
+        if (MASK & MASK_BLOCK) {
+            // fragments of one 16-key step at a time (register pressure, as in qk)
+#pragma unroll
+            for (int ks = 0; ks < BN / 16; ++ks) {
+                u32x4 va[DB];
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][0]));
+                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][1]));
+                    const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi4);
+                    va[db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                }
+                const int kb = ks >> 1, o4 = 4 * (ks & 1);
+                const V8 pf = as_vec<V8>(u32x4{pp[kb][o4], pp[kb][o4 + 1], pp[kb][o4 + 2], pp[kb][o4 + 3]});
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(as_vec<V8>(va[db]), pf, oacc[db]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < BN / 16; ++ks) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 1);  // transposed V reads
+                __builtin_amdgcn_sched_group_barrier(0x008, DB, 1);      // their MFMAs
+            }
+            return;
+        }
+        u32x4 va[BN / 16][DB];
+#pragma unroll
+        for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][0]));
+                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (MM_LDS s16x4 *)(Vt + ks * 16 * TL::ROWB + voff[db][1]));
+                const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi4);
+                va[ks][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            }
+#pragma unroll
+        for (int ks = 0; ks < BN / 16; ++ks) {
+            const int kb = ks >> 1, o4 = 4 * (ks & 1);
+            const V8 pf = as_vec<V8>(u32x4{pp[kb][o4], pp[kb][o4 + 1], pp[kb][o4 + 2], pp[kb][o4 + 3]});
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(as_vec<V8>(va[ks][db]), pf, oacc[db]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (BN / 16) * DB, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, (BN / 16) * DB, 1);
+    };
+
+    // one tile, all phases in order: DMA tile `next` (if >= 0) into (Kn, Vn) while
+    // computing tile kt on (Kt, Vt)
+    auto tile = [&](int kt, int blk, const unsigned char *Kt, const unsigned char *Vt, int next,
+                    unsigned char *Kn, unsigned char *Vn) {
+        if (next >= 0) load_tile(next, Kn, Vn);
+        bool need_mask;
+        if (!classify(kt, blk, need_mask)) {
+            f32x16 sacc[NKB];
+            qk(Kt, sacc);
+            uint32_t pp[NKB][8];
+            softmax(kt, blk, need_mask, sacc, pp);
+            pv(Vt, pp);
         }
     };
 
@@ -433,9 +499,7 @@ void fwd_mfma_kernel(FwdParams p) {
     }
 }
 
-#ifndef MM_FWD_NW
-#define MM_FWD_NW 8  // waves per workgroup without a mask mod
-#endif
+
 #ifndef MM_FWD_NW_MASKED
 #define MM_FWD_NW_MASKED 4  // with causal / window masks: finer row tiles skip more keys
 #endif
