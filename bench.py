@@ -355,6 +355,12 @@ def main():
         specs["block_causal"] = dict(causal=True, block_mask=bm_causal)
         specs["block_sparse_50"] = dict(block_mask=bm_rand)
         block_pairs = int((bm_rand_np != 0).sum()) * mm.BLOCK_Q * mm.BLOCK_KV
+        # document mask (packed sequences, a mask_mod over captured id tensors): 16
+        # documents of random lengths per sequence, causal inside each document
+        docs_np = inputs.packed_document_ids(7, B, S, 16)
+        specs["document_causal"] = dict(causal=True, q_doc=torch.from_numpy(docs_np).to(dev))
+        doc_pairs = H * sum(int(n) * (int(n) + 1) // 2
+                            for row in docs_np for n in np.unique(row, return_counts=True)[1])
         # fp8 (e4m3) inputs: the same draws quantised per tensor on the device
         (q8, sq), (k8, sk), (v8, sv) = (to_fp8(t, torch) for t in (q, k, v))
         fp8_kw = dict(q=q8, k=k8, v=v8, descale=(sq, sk, sv))
@@ -380,6 +386,8 @@ def main():
                 alg = 4.0 * D * block_pairs  # block_pairs: kept pairs summed over (b, h)
             elif name == "sliding_window":
                 alg = 4.0 * B * H * D * window_pairs(S, W)
+            elif name == "document_causal":
+                alg = 4.0 * D * doc_pairs  # kept pairs summed over (b, h)
             else:
                 alg = dense
             ent = {"us": round(t * 1e6, 1), "tflops_dense_equiv": round(dense / t / 1e12, 1),
@@ -476,7 +484,10 @@ def main():
         bws = torch.empty(mm.bwd_workspace_size(B, H, S) // 4 + 4, dtype=torch.float32, device=dev)
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         bwd = {}
-        for name, kw in (("no_mod", {}), ("causal", dict(causal=True))):
+        bcases = [("no_mod", {}), ("causal", dict(causal=True))]
+        if "document_causal" in cases:
+            bcases.append(("document_causal", dict(causal=True, q_doc=torch.from_numpy(docs_np).to(dev))))
+        for name, kw in bcases:
             o_b = torch.empty_like(q)
             l_b = torch.empty(B, H, S, dtype=torch.float32, device=dev)
             mm.attn_fwd(q, k, v, scale, out=o_b, lse=l_b, **kw)
@@ -494,11 +505,15 @@ def main():
             t = e0.elapsed_time(e1) / n * 1e-3
             # five products of the forward's size (S and dP recomputed, dV, dK, dQ):
             # 2.5 x the forward's flops (half for causal)
-            alg = 2.5 * fwd_flops(B, H, S, S, D) * (0.5 if kw else 1.0)
+            if name == "document_causal":
+                alg = 2.5 * 4.0 * D * doc_pairs
+            else:
+                alg = 2.5 * fwd_flops(B, H, S, S, D) * (0.5 if kw else 1.0)
             bwd[name] = {"us": round(t * 1e6, 1), "tflops_algorithmic": round(alg / t / 1e12, 1),
                          "frac_bf16_peak": round(alg / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         res["bwd"] = {"workload": "bf16 B2 H32 D128 S8192, dq/dk/dv from the forward's O and LSE",
-                      "algorithmic": "2.5 x 4*B*H*S*S*D flop (five S-sized products; causal half)",
+                      "algorithmic": "2.5 x 4*B*H*S*S*D flop (five S-sized products; causal half; "
+                                     "documents: 2.5 x 4*D per kept pair)",
                       **bwd}
     if "fp8_no_mod" in cases:
         c8 = cases["fp8_no_mod"]
