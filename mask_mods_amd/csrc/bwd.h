@@ -114,8 +114,10 @@ void bwd_dq_kernel(BwdParams p) {
     if (MASK & MASK_DOC) {
         const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
         if (!(MASK & MASK_BLOCK)) {
-            j_lo = max(j_lo, doc_lower(kd, p.Skv, qd[q0]));
-            j_hi = min(j_hi, doc_upper(kd, p.Skv, qd[row_max]));
+            int dlo, dhi;
+            wave_search_range(kd, p.Skv, qd[q0], qd[row_max], lane, dlo, dhi);
+            j_lo = max(j_lo, dlo);
+            j_hi = min(j_hi, dhi);
         }
         wd_lo = qd[min(r0, p.Sq - 1)];
         wd_hi = qd[min(r0 + 31, p.Sq - 1)];
@@ -195,13 +197,19 @@ void bwd_dq_kernel(BwdParams p) {
             skip |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
+        bool doc_mask = false;
         if ((MASK & MASK_DOC) && pred && !skip) {
             const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
             const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
             skip |= kdh < wd_lo || kdl > wd_hi;
-            need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
+            doc_mask = !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
+            need_mask |= doc_mask;
         }
         if (skip) return;
+        // a tile that straddles documents: the lane's document's keys, [dfirst, dend)
+        int dfirst = 0, dend = BN;
+        if ((MASK & MASK_DOC) && doc_mask)
+            tile_doc_range(p.kvdoc[b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1)], mydoc, dfirst, dend);
         // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T, then dS^T, then
         // dQ^T += K^T dS^T over the block's two 16-key k-steps
         const bool general = ALIBI || need_mask;
@@ -233,8 +241,7 @@ void bwd_dq_kernel(BwdParams p) {
                             bool keep = j < p.Skv;
                             if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
                             if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                            if ((MASK & MASK_DOC) && pred)
-                                keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
+                            if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
                             pv = keep ? fast_exp2(t - lse2) : 0.f;
                         } else {
                             pv = fast_exp2(fmaf(sacc[e], c2, -lse2));
@@ -371,8 +378,10 @@ void bwd_dkdv_kernel(BwdParams p) {
     if ((MASK & MASK_DOC) && p.Skv > 0) {
         const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
         if (!(MASK & MASK_BLOCK)) {
-            i_lo = max(i_lo, doc_lower(qd, p.Sq, kd[kmin]));
-            i_hi = min(i_hi, doc_upper(qd, p.Sq, kd[kmax]));
+            int dlo, dhi;
+            wave_search_range(qd, p.Sq, kd[kmin], kd[kmax], lane, dlo, dhi);
+            i_lo = max(i_lo, dlo);
+            i_hi = min(i_hi, dhi);
         }
         wk_lo = kd[min(kw0, p.Skv - 1)];
         wk_hi = kd[min(kw0 + 31, p.Skv - 1)];
@@ -468,13 +477,20 @@ void bwd_dkdv_kernel(BwdParams p) {
             skip |= (kw0 - i_last > p.window) || (i0 - (kw0 + 31) > p.window);
             need_mask |= max(i_last - kw0, kw0 + 31 - i0) > p.window;
         }
+        bool doc_mask = false;
         if ((MASK & MASK_DOC) && pred && !skip) {
             const int32_t *qd = p.qdoc + b * p.qdoc_sb;
             const int qdl = qd[i0], qdh = qd[min(i_last, p.Sq - 1)];
             skip |= qdh < wk_lo || qdl > wk_hi;
-            need_mask |= !(wk_lo == wk_hi && qdl == qdh && qdl == wk_lo);
+            doc_mask = !(wk_lo == wk_hi && qdl == qdh && qdl == wk_lo);
+            need_mask |= doc_mask;
         }
         if (skip) return;
+        // a tile that straddles documents: the rows of the lane's key's document,
+        // [dfirst, dend) as offsets in the 64-row tile
+        int dfirst = 0, dend = BQ;
+        if ((MASK & MASK_DOC) && doc_mask)
+            tile_doc_range(p.qdoc[b * p.qdoc_sb + min(i0 + lane, p.Sq - 1)], mykdoc, dfirst, dend);
         // per-lane rows of block rb of the accumulator: i0 + 32*rb + 8*a + 4*hi + (0..3),
         // their lse2 and D from the copy in LDS (pad rows hold no data and are masked)
         const float *sl2 = (const float *)(Qt + 2 * TILEB), *sdd = sl2 + BQ;
@@ -522,8 +538,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                             bool keep = key_ok && i < p.Sq;
                             if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
                             if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
-                            if ((MASK & MASK_DOC) && pred)
-                                keep &= p.qdoc[b * p.qdoc_sb + min(i, p.Sq - 1)] == mykdoc;
+                            if ((MASK & MASK_DOC) && pred) keep &= i - i0 >= dfirst && i - i0 < dend;
                             x = keep ? fast_exp2(t - lse2) : 0.f;
                             ds[u] = keep ? x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]) : 0.f;
                         } else {

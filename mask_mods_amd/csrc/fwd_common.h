@@ -56,6 +56,66 @@ __device__ __forceinline__ void kv_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Wave-wide search on a non-decreasing int32 array of n entries for both ends of a
+// range: the first index whose value is >= vlo and the first whose value is > vhi (n if
+// none). n, vlo and vhi are wave-uniform and every lane of the wave takes part. Each
+// round probes up to 64 evenly spaced entries per search (one load per lane); the
+// probes that lie before the answer form a prefix, counted with a ballot, and the answer
+// lies between the last of them and the next probe. 8192 entries take three rounds,
+// the two searches sharing them so that their loads are in flight together.
+__device__ __forceinline__ void wave_search_range(const int32_t *a, int n, int vlo, int vhi, int lane,
+                                                  int &out_lo, int &out_hi) {
+    int lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
+    while (lo1 < hi1 || lo2 < hi2) {
+        const int st1 = (hi1 - lo1 + 63) >> 6, st2 = (hi2 - lo2 + 63) >> 6;
+        const int i1 = lo1 + lane * st1, i2 = lo2 + lane * st2;
+        const int x1 = lo1 < hi1 ? a[min(i1, hi1 - 1)] : 0;
+        const int x2 = lo2 < hi2 ? a[min(i2, hi2 - 1)] : 0;
+        const int c1 = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i1 < hi1 && x1 < vlo));
+        const int c2 = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i2 < hi2 && x2 <= vhi));
+        if (lo1 < hi1) {
+            if (c1 == 0) hi1 = lo1;
+            else {
+                const int h = min(lo1 + c1 * st1, hi1);
+                lo1 = lo1 + (c1 - 1) * st1 + 1;
+                hi1 = h;
+            }
+        }
+        if (lo2 < hi2) {
+            if (c2 == 0) hi2 = lo2;
+            else {
+                const int h = min(lo2 + c2 * st2, hi2);
+                lo2 = lo2 + (c2 - 1) * st2 + 1;
+                hi2 = h;
+            }
+        }
+    }
+    out_lo = lo1;
+    out_hi = lo2;
+}
+
+// The keys of one 64-key tile that share a row's document, for documents whose ids do
+// not decrease along the keys: lane l holds t = the id of key k0 + l (clamped to the last
+// key), and `mine` is the id of the lane's row. Sets [first, end) to the lane's
+// document's keys as offsets in the tile. The loop visits each distinct document among
+// the wave's rows once (rows are sorted too), starting from the first lane's.
+__device__ __forceinline__ void tile_doc_range(int t, int mine, int &first, int &end) {
+    first = 0;
+    end = 0;
+    int d = __builtin_amdgcn_readfirstlane(mine);
+    for (;;) {
+        const int a = __builtin_popcountll(__builtin_amdgcn_ballot_w64(t < d));
+        const int e = __builtin_popcountll(__builtin_amdgcn_ballot_w64(t <= d));
+        if (mine == d) {
+            first = a;
+            end = e;
+        }
+        const uint64_t later = __builtin_amdgcn_ballot_w64(mine > d);
+        if (later == 0) break;
+        d = __builtin_amdgcn_readlane(mine, __builtin_ctzll(later));
+    }
+}
+
 // Walks the non-empty entries of one row of a block-mask table (one byte per key tile).
 // The row is read 64 bytes at a time (one per lane) into a register window; a ballot of
 // the nonzero bytes gives a wave-uniform bitmap, so every wave of a workgroup finds the

@@ -123,8 +123,10 @@ void fwd_fp8_kernel(FwdParams p) {
         // packed documents: only keys whose document lies within the tile's rows' range
         const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
         if (!(MASK & MASK_BLOCK)) {
-            j_lo = max(j_lo, doc_lower(kd, p.Skv, qd[q0]));
-            j_hi = min(j_hi, doc_upper(kd, p.Skv, qd[row_max]));
+            int dlo, dhi;
+            wave_search_range(kd, p.Skv, qd[q0], qd[row_max], lane, dlo, dhi);
+            j_lo = max(j_lo, dlo);
+            j_hi = min(j_hi, dhi);
         }
     }
     // document ids of the wave's first and last rows and of the lane's row
@@ -236,14 +238,20 @@ void fwd_fp8_kernel(FwdParams p) {
             dead |= (k0 - r_last > p.window) || (r0 - (k0 + BN - 1) > p.window);
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
+        bool doc_mask = false;
         if ((MASK & MASK_DOC) && pred) {
             const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
             const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
             dead |= kdh < wd_lo || kdl > wd_hi;
+            doc_mask = !dead && !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
             need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
         }
         if (!(ALIBI || need_mask || !(c2 > 0.f))) return c2;
         const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
+        // a tile that straddles documents: the lane's document's keys, [dfirst, dend)
+        int dfirst = 0, dend = BN;
+        if ((MASK & MASK_DOC) && doc_mask)
+            tile_doc_range(p.kvdoc[b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1)], mydoc, dfirst, dend);
         auto scores = [&](bool masked) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -256,8 +264,7 @@ void fwd_fp8_kernel(FwdParams p) {
                         bool keep = (j < p.Skv) & !dead;
                         if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
                         if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                        if ((MASK & MASK_DOC) && pred)
-                            keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
+                        if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
                         t = keep ? t : -INFINITY;
                     }
                     sacc[kb][e] = t;

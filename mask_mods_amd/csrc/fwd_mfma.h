@@ -141,8 +141,10 @@ void fwd_mfma_kernel(FwdParams p) {
         // packed documents: only keys whose document lies within the tile's rows' range
         const int32_t *qd = p.qdoc + b * p.qdoc_sb, *kd = p.kvdoc + b * p.kvdoc_sb;
         if (!(MASK & MASK_BLOCK)) {
-            j_lo = max(j_lo, doc_lower(kd, p.Skv, qd[q0]));
-            j_hi = min(j_hi, doc_upper(kd, p.Skv, qd[row_max]));
+            int dlo, dhi;
+            wave_search_range(kd, p.Skv, qd[q0], qd[row_max], lane, dlo, dhi);
+            j_lo = max(j_lo, dlo);
+            j_hi = min(j_hi, dhi);
         }
     }
     // document ids of the wave's first and last rows and of the lane's row
@@ -230,12 +232,13 @@ void fwd_mfma_kernel(FwdParams p) {
     // Whether this wave skips tile kt, and whether the tile needs per-pair masking.
     // `blk` is the tile's block-mask class: 1 = the mask_mod predicates decide,
     // 2 = every pair kept (predicates not evaluated).
-    auto classify = [&](int kt, int blk, bool &need_mask) -> bool {
+    auto classify = [&](int kt, int blk, bool &need_mask, bool &doc_mask) -> bool {
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
         const bool pred = blk == 1;  // predicates apply in this tile
         bool skip = kt >= kt_hi;
         need_mask = k0 + BN > p.Skv;
+        doc_mask = false;
         if ((MASK & MASK_CAUSAL) && pred) {
             skip |= k0 > r_last;
             need_mask |= k0 + BN - 1 > r0;
@@ -248,7 +251,8 @@ void fwd_mfma_kernel(FwdParams p) {
             const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
             const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
             skip |= kdh < wd_lo || kdl > wd_hi;
-            need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
+            doc_mask = !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
+            need_mask |= doc_mask;
         }
         return skip;
     };
@@ -291,7 +295,9 @@ void fwd_mfma_kernel(FwdParams p) {
     };
     // scale, score_mod and mask_mod, the running max (lazily rescaling O and l), then
     // P = 2^(t - m) as 16-bit pairs and the row sum
-    auto softmax = [&](int kt, int blk, bool need_mask, f32x16 (&sacc)[NKB], uint32_t (&pp)[NKB][8]) {
+    // tdoc: with doc_mask, the document id of key k0 + lane (clamped to the last key)
+    auto softmax = [&](int kt, int blk, bool need_mask, bool doc_mask, int tdoc, f32x16 (&sacc)[NKB],
+                       uint32_t (&pp)[NKB][8]) {
         const int k0 = kt * BN;
         const bool pred = blk == 1;
         // scores in base-2 units; lane's keys: k0 + 32*kb + 8*(e/4) + 4*hi + e%4.
@@ -302,6 +308,9 @@ void fwd_mfma_kernel(FwdParams p) {
         const bool general = ALIBI || need_mask || !(c2 > 0.f);
         if (general) {
             const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
+            // the lane's document's keys in this tile, [dfirst, dend) as tile offsets
+            int dfirst = 0, dend = BN;
+            if ((MASK & MASK_DOC) && doc_mask) tile_doc_range(tdoc, mydoc, dfirst, dend);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -313,8 +322,7 @@ void fwd_mfma_kernel(FwdParams p) {
                         bool keep = j < p.Skv;
                         if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
                         if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                        if ((MASK & MASK_DOC) && pred)
-                            keep &= p.kvdoc[b * p.kvdoc_sb + min(j, p.Skv - 1)] == mydoc;
+                        if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
                         t = keep ? t : -INFINITY;
                     }
                     sacc[kb][e] = t;
@@ -413,12 +421,16 @@ void fwd_mfma_kernel(FwdParams p) {
     auto tile = [&](int kt, int blk, const unsigned char *Kt, const unsigned char *Vt, int next,
                     unsigned char *Kn, unsigned char *Vn) {
         if (next >= 0) load_tile(next, Kn, Vn);
-        bool need_mask;
-        if (!classify(kt, blk, need_mask)) {
+        bool need_mask, doc_mask;
+        if (!classify(kt, blk, need_mask, doc_mask)) {
+            // a tile that straddles documents: its 64 key ids, loaded before the QK
+            // products so that the load is in flight while they run
+            int tdoc = 0;
+            if ((MASK & MASK_DOC) && doc_mask) tdoc = p.kvdoc[b * p.kvdoc_sb + min(kt * BN + lane, p.Skv - 1)];
             f32x16 sacc[NKB];
             qk(Kt, sacc);
             uint32_t pp[NKB][8];
-            softmax(kt, blk, need_mask, sacc, pp);
+            softmax(kt, blk, need_mask, doc_mask, tdoc, sacc, pp);
             pv(Vt, pp);
         }
     };
