@@ -203,3 +203,9 @@ def test_document_mask_2048_sampled_heads():
                                    q_doc=docs[b:b + 1])
         for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
             assert_parity(to_f64(got[sl]), want, O_ATOL, O_RTOL, f"{name}[{b},{h}]")
+
+
+def test_document_mask_sparse_ids():
+    base = inputs.packed_document_ids(36, 1, 300, 5)[0]
+    docs = np.array([-9, 3, 4, 70000, 2 ** 31 - 1], dtype=np.int64)[base].astype(np.int32)[None]
+    _check(1, 2, 2, 300, 300, 64, "bf16", seed=36, causal=True, q_doc=docs)

@@ -183,3 +183,13 @@ def test_config_8192_sampled(causal):
     docs = inputs.packed_document_ids(14, B, S, 16)
     rows = inputs.sample_rows(14, B, H, S, n_random=64)
     _run(B, H, H, S, S, D, "bf16", docs, seed=14, causal=causal, rows=rows)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sparse_negative_and_large_ids(causal):
+    """Ids need only be non-decreasing: gaps, negative values and values near the int32
+    limit behave like 0, 1, 2, ... (the kernels visit only the ids present)."""
+    base = inputs.packed_document_ids(15, 1, 600, 7)[0]
+    remap = np.array([-2 ** 31, -7, 0, 1000, 10 ** 6, 2 ** 30, 2 ** 31 - 1], dtype=np.int64)
+    docs = remap[base].astype(np.int32)[None]
+    _run(1, 2, 2, 600, 600, 128, "bf16", docs, seed=15, causal=causal)
