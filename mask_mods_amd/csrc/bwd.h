@@ -602,6 +602,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 template <typename TT, int D, bool A, int M>
 hipError_t launch_bwd_one(BwdParams p, hipStream_t s) {
     constexpr int NW = 4;
+    // dQ workgroup: 8 waves (256 rows share each K/V tile) without a mask, as in the
+    // forward (1% faster overall at S = 8192); masks keep 128-row tiles
+    constexpr int NWQ = M == 0 ? 8 : 4;
     const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
     if (nrows > 0) {
         const int rpb = 256 / (D / 8);
@@ -609,8 +612,8 @@ hipError_t launch_bwd_one(BwdParams p, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         BwdParams q = p;
-        q.n_tiles = (p.Sq + 32 * NW - 1) / (32 * NW);
-        bwd_dq_kernel<TT, D, A, M, NW><<<dim3((unsigned)(q.n_tiles * p.Hq * p.B)), dim3(64 * NW), 0, s>>>(q);
+        q.n_tiles = (p.Sq + 32 * NWQ - 1) / (32 * NWQ);
+        bwd_dq_kernel<TT, D, A, M, NWQ><<<dim3((unsigned)(q.n_tiles * p.Hq * p.B)), dim3(64 * NWQ), 0, s>>>(q);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
