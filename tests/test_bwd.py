@@ -209,3 +209,17 @@ def test_document_mask_sparse_ids():
     base = inputs.packed_document_ids(36, 1, 300, 5)[0]
     docs = np.array([-9, 3, 4, 70000, 2 ** 31 - 1], dtype=np.int64)[base].astype(np.int32)[None]
     _check(1, 2, 2, 300, 300, 64, "bf16", seed=36, causal=True, q_doc=docs)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_config_8192_one_sampled_head(causal):
+    """B2 H32 D128 S8192, the shape bench.py times, on the GPU; the oracle recomputes one
+    full (b, h) head (about half a minute of CPU)."""
+    B, H, S, D = 2, 32, 8192, 128
+    (dq, dk, dv), (qd, kd, vd, dod), scale = _grads(B, H, H, S, S, D, "bf16", seed=37, causal=causal)
+    b, h = (1, 17) if causal else (0, 6)
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    ref = oracle.attention_bwd(qd[sl], kd[sl], vd[sl], dod[sl], scale=scale, causal=causal)
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        err = assert_parity(to_f64(got[sl]), want, O_ATOL, O_RTOL, f"{name}[{b},{h}]")
+        print(f"[bwd] 8192 {name} max|err| {err:.3e}", flush=True)
