@@ -79,9 +79,13 @@ enum {
     MM_MASK_DOCUMENT = 8u /* keep iff q_doc_ids[b][q_idx] == kv_doc_ids[b][kv_idx]: a
                              mask_mod that captures tensors (packed documents). The ids
                              must not decrease along the positions of a sequence (the
-                             kernels skip whole tiles from the end ids). Composes with
-                             MM_MASK_CAUSAL, MM_MASK_ROWDROP and the block mask; not
-                             with MM_MASK_WINDOW (MM_ERR_UNSUPPORTED)                   */
+                             kernels skip whole tiles from the end ids); any int32
+                             values, gaps allowed. Ids that do decrease give an
+                             unspecified result, though every read stays within the
+                             arrays. Composes with MM_MASK_CAUSAL, MM_MASK_ROWDROP and
+                             the block mask (inside partial blocks); not with
+                             MM_MASK_WINDOW (MM_ERR_UNSUPPORTED). Forward and backward
+                             only (decode takes an additive mask instead)              */
 };
 
 /*
@@ -109,9 +113,13 @@ typedef struct mm_mods {
     const float *alibi_slopes;    /* device fp32 [Hq], or NULL for 2^(-8(h+1)/Hq)      */
     const uint8_t *block_mask;    /* device block mask (above), or NULL for none       */
     int64_t block_mask_strides[3];/* elements (bytes), for b, h, query block; >= 0     */
-    const int32_t *q_doc_ids;     /* MM_MASK_DOCUMENT: device int32 [B, >= Sq]          */
-    const int32_t *kv_doc_ids;    /* MM_MASK_DOCUMENT: device int32 [B, >= Skv]         */
-    int64_t doc_strides[2];       /* elements between sequences of q / kv ids; >= 0    */
+    const int32_t *q_doc_ids;     /* MM_MASK_DOCUMENT: device int32 [B, >= Sq], 4-byte
+                                     aligned, contiguous along the sequence; required
+                                     when B*Sq*Skv > 0 (MM_ERR_NULL), else unused       */
+    const int32_t *kv_doc_ids;    /* MM_MASK_DOCUMENT: device int32 [B, >= Skv], same   */
+    int64_t doc_strides[2];       /* elements between the sequences of q / kv ids, >= 0
+                                     (MM_ERR_STRIDE); 0 shares one sequence's ids over
+                                     the batch                                          */
 } mm_mods;
 
 typedef struct mm_fwd_args {
