@@ -213,3 +213,9 @@ def test_paged_gqa_no_mask_forced_splits():
 
 def test_paged_long_and_empty():
     _paged_run(2, 16, 16, [32768, 0], 64, "f16", 128, seed=17)
+
+
+def test_long_cache_262144_gqa():
+    """A 262144-position cache (256 splits, the most the split count allows), GQA 4:1,
+    with the pad mask and a capacity above the length."""
+    _run(1, 8, 2, [262144 - 77], 128, "f16", Scap=262144, use_lens=False)

@@ -228,3 +228,13 @@ def test_config_gqa_cross_rowdrop(dtype, window):
     o = to_f64(out).reshape(-1, 128)
     assert np.all(l[dropped] == -np.inf) and np.all(o[dropped] == 0)
     assert np.all(np.isfinite(l[~dropped]))
+
+
+# ---------------------------------------------------------------- long sequences
+@pytest.mark.parametrize("mods", [dict(causal=True), dict(alibi=True, causal=True), dict()])
+def test_long_sequence_65536_sampled(mods):
+    """65536 queries and keys (GQA 2:1): row and key indices, byte offsets and the alibi
+    distances well past the benchmark's 8192; first/last rows of each head plus random
+    rows against the oracle."""
+    S = 65536
+    _run(1, 2, 1, S, S, 128, "bf16", seed=21, rows=inputs.sample_rows(21, 1, 2, S, n_random=24), **mods)
