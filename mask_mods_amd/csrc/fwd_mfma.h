@@ -515,17 +515,22 @@ void fwd_mfma_kernel(FwdParams p) {
 #ifndef MM_FWD_NW_MASKED
 #define MM_FWD_NW_MASKED 4  // with causal / window masks: finer row tiles skip more keys
 #endif
+#ifndef MM_FWD_NW_CAUSAL
+#define MM_FWD_NW_CAUSAL 8  // causal alone: the shared tiles outweigh the idle diagonal waves
+#endif
 #ifndef MM_FWD_NST
 #define MM_FWD_NST 2
 #endif
 
 template <typename TT, int D, bool A, int M>
 hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
-    // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic; with
-    // causal or window masks, 4-wave tiles (128 rows) follow the diagonal / band more
-    // closely and skip more key tiles, which matters more; a block mask's q-blocks are
-    // 128 rows, one 4-wave workgroup each
-    constexpr int NW = M == 0 ? MM_FWD_NW : MM_FWD_NW_MASKED, NST = MM_FWD_NST;
+    // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic. Causal
+    // alone keeps 8 (1.5% faster at S = 8192 than 4 despite the waves idle past the
+    // diagonal); with a window or documents, 4-wave tiles (128 rows) follow the band
+    // more closely and skip more key tiles, which matters more; a block mask's q-blocks
+    // are 128 rows, one 4-wave workgroup each
+    constexpr int NW = M == 0 ? MM_FWD_NW : (M == MASK_CAUSAL ? MM_FWD_NW_CAUSAL : MM_FWD_NW_MASKED),
+                  NST = MM_FWD_NST;
     static_assert(!(M & MASK_BLOCK) || NW == 4, "block masks use 128-row workgroups");
     p.n_qtiles = (p.Sq + 32 * NW - 1) / (32 * NW);
     const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(64 * NW);
