@@ -602,9 +602,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 template <typename TT, int D, bool A, int M>
 hipError_t launch_bwd_one(BwdParams p, hipStream_t s) {
     constexpr int NW = 4;
-    // dQ workgroup: 8 waves (256 rows share each K/V tile) without a mask, as in the
-    // forward (1% faster overall at S = 8192); masks keep 128-row tiles
-    constexpr int NWQ = M == 0 ? 8 : 4;
+    // dQ workgroup: 8 waves (256 rows share each K/V tile) without a mask or with
+    // causal alone, as in the forward (each 1-1.5% faster overall at S = 8192); other
+    // masks keep 128-row tiles
+    constexpr int NWQ = (M == 0 || M == MASK_CAUSAL) ? 8 : 4;
     const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
     if (nrows > 0) {
         const int rpb = 256 / (D / 8);

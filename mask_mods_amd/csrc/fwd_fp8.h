@@ -446,7 +446,7 @@ void fwd_fp8_kernel(FwdParams p) {
 
 template <int D, bool A, int M>
 hipError_t launch_fwd_fp8_one(FwdParams p, hipStream_t s) {
-    constexpr int NW = M == 0 ? 8 : 4;
+    constexpr int NW = M == 0 ? 8 : 4;  // (8 waves for causal: 7% slower)
     p.n_qtiles = (p.Sq + 32 * NW - 1) / (32 * NW);
     const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(64 * NW);
     fwd_fp8_kernel<D, A, M, NW><<<grid, block, 0, s>>>(p);
