@@ -513,7 +513,7 @@ void fwd_mfma_kernel(FwdParams p) {
 
 
 #ifndef MM_FWD_NW_MASKED
-#define MM_FWD_NW_MASKED 4  // with causal / window masks: finer row tiles skip more keys
+#define MM_FWD_NW_MASKED 4  // window, document or block masks: finer row tiles skip more keys
 #endif
 #ifndef MM_FWD_NW_CAUSAL
 #define MM_FWD_NW_CAUSAL 8  // causal alone: the shared tiles outweigh the idle diagonal waves
