@@ -82,10 +82,10 @@ enum {
                              kernels skip whole tiles from the end ids); any int32
                              values, gaps allowed. Ids that do decrease give an
                              unspecified result, though every read stays within the
-                             arrays. Composes with MM_MASK_CAUSAL, MM_MASK_ROWDROP and
-                             the block mask (inside partial blocks); not with
-                             MM_MASK_WINDOW (MM_ERR_UNSUPPORTED). Forward and backward
-                             only (decode takes an additive mask instead)              */
+                             arrays. Composes with MM_MASK_CAUSAL, MM_MASK_WINDOW,
+                             MM_MASK_ROWDROP and the block mask (inside partial
+                             blocks). Forward and backward only (decode takes an
+                             additive mask instead)                                     */
 };
 
 /*

@@ -222,7 +222,7 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
     (all kept); size-1 leading dims broadcast.
     q_doc, kv_doc: document mask, int32 device tensors [B|1, >=Sq] and [B|1, >=Skv] of
     ids that do not decrease along the sequence (kv_doc defaults to q_doc): a pair is
-    kept only where the two ids are equal. Not combinable with ``window``.
+    kept only where the two ids are equal (AND-composed with the other mods).
     Returns (out, lse) with lse fp32 [B,Hq,Sq] (None if return_lse is False).
     """
     torch = _torch()

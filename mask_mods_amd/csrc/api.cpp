@@ -32,10 +32,9 @@ bool strides_not_mult(const int64_t *s, int n, int m) {
 }
 
 // The document mask's id arrays: both present (when any pair exists), 4-byte aligned,
-// non-negative strides; not composed with the window.
+// non-negative strides.
 mm_status check_doc(const mm_mods &m, bool pairs) {
     if (!(m.mask_flags & MM_MASK_DOCUMENT)) return MM_OK;
-    if (m.mask_flags & MM_MASK_WINDOW) return MM_ERR_UNSUPPORTED;
     if (pairs && (!m.q_doc_ids || !m.kv_doc_ids)) return MM_ERR_NULL;
     if (bad_strides(m.doc_strides, 2)) return MM_ERR_STRIDE;
     if (((uintptr_t)m.q_doc_ids | (uintptr_t)m.kv_doc_ids) & 3u) return MM_ERR_STRIDE;

@@ -459,10 +459,12 @@ hipError_t launch_fwd_fp8(const FwdParams &p, bool alibi, int mask, hipStream_t 
     switch ((alibi ? 16 : 0) + (mask & 15)) {
         MM_CASE(0, 0) MM_CASE(0, 1) MM_CASE(0, 2) MM_CASE(0, 3)
         MM_CASE(0, 4) MM_CASE(0, 5) MM_CASE(0, 6) MM_CASE(0, 7)
-        MM_CASE(0, 8) MM_CASE(0, 9) MM_CASE(0, 12) MM_CASE(0, 13)
+        MM_CASE(0, 8) MM_CASE(0, 9) MM_CASE(0, 10) MM_CASE(0, 11)
+        MM_CASE(0, 12) MM_CASE(0, 13) MM_CASE(0, 14) MM_CASE(0, 15)
         MM_CASE(1, 0) MM_CASE(1, 1) MM_CASE(1, 2) MM_CASE(1, 3)
         MM_CASE(1, 4) MM_CASE(1, 5) MM_CASE(1, 6) MM_CASE(1, 7)
-        MM_CASE(1, 8) MM_CASE(1, 9) MM_CASE(1, 12) MM_CASE(1, 13)
+        MM_CASE(1, 8) MM_CASE(1, 9) MM_CASE(1, 10) MM_CASE(1, 11)
+        MM_CASE(1, 12) MM_CASE(1, 13) MM_CASE(1, 14) MM_CASE(1, 15)
         default: return hipErrorInvalidValue;
     }
 #undef MM_CASE

@@ -202,7 +202,7 @@ BAD_Q_STRIDE = dict(q_strides=mm._I64x3(-1, 0, 0))
 @pytest.mark.parametrize("kw,status", [
     (dict(mods_mask_flags=8), NULL),                               # ids missing
     (dict(DOC, mods_kv_doc_ids=None), NULL),
-    (dict(DOC, mods_mask_flags=8 | 2, mods_window=4), UNSUP),      # not with the window
+    (dict(DOC, mods_mask_flags=8 | 2, mods_window=4, **BAD_Q_STRIDE), STRIDE),  # with the window
     (dict(DOC, mods_doc_strides=mm._I64x2(0, -16)), STRIDE),
     (dict(DOC, mods_q_doc_ids=FAKE + 2), STRIDE),                  # int32 alignment
     (dict(DOC, **BAD_Q_STRIDE), STRIDE),                           # ids accepted: reaches the stride check
@@ -244,7 +244,7 @@ def _bwd(**kw):
     (dict(workspace=None), WORKSPACE),
     (dict(workspace_bytes=8), WORKSPACE),
     (dict(mods_mask_flags=8), NULL),
-    (dict(DOC, mods_mask_flags=8 | 2), UNSUP),
+    (dict(DOC, mods_mask_flags=8 | 2, do_strides=mm._I64x3(0, 0, 12)), STRIDE),
     (dict(DOC, mods_doc_strides=mm._I64x2(-1, 0)), STRIDE),
     (dict(DOC, do_strides=mm._I64x3(0, 0, 12)), STRIDE),
     (dict(B=0), OK),

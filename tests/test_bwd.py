@@ -223,3 +223,10 @@ def test_config_8192_one_sampled_head(causal):
     for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         err = assert_parity(to_f64(got[sl]), want, O_ATOL, O_RTOL, f"{name}[{b},{h}]")
         print(f"[bwd] 8192 {name} max|err| {err:.3e}", flush=True)
+
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_document_mask_with_window(causal):
+    docs = inputs.packed_document_ids(38, 1, 384, 4)
+    _check(1, 4, 2, 384, 384, 128, "bf16", seed=38, window=70, causal=causal, q_doc=docs)

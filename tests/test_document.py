@@ -26,18 +26,18 @@ def _ids(ids):
 
 
 def _run(B, Hq, Hkv, Sq, Skv, D, dtype, q_doc, kv_doc=None, *, causal=False, alibi=False,
-         rowdrop=False, block_mask=None, seed=0, rows=None):
+         rowdrop=False, block_mask=None, window=None, seed=0, rows=None):
     """q_doc / kv_doc: int32 numpy [B|1, S] (kv_doc None: the query ids serve both)."""
     import torch
     import mask_mods_amd as mm
     print(f"[doc] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {dtype} q_doc={q_doc.shape} "
           f"kv_doc={None if kv_doc is None else kv_doc.shape} causal={causal} alibi={alibi} "
-          f"rowdrop={rowdrop} block={block_mask is not None} seed={seed}", flush=True)
+          f"rowdrop={rowdrop} block={block_mask is not None} window={window} seed={seed}", flush=True)
     x = inputs.attention_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
     q, k, v = (to_torch(x[n], dtype) for n in ("q", "k", "v"))
     scale = float(np.float32(1.0 / math.sqrt(D)))
     bm = torch.from_numpy(block_mask).cuda() if block_mask is not None else None
-    out, lse = mm.attn_fwd(q, k, v, scale, causal=causal,
+    out, lse = mm.attn_fwd(q, k, v, scale, causal=causal, window=window,
                            score_mod=mm.SCORE_ALIBI if alibi else mm.SCORE_NONE,
                            rowdrop=RD if rowdrop else None, block_mask=bm,
                            q_doc=_ids(q_doc), kv_doc=_ids(kv_doc))
@@ -45,7 +45,7 @@ def _run(B, Hq, Hkv, Sq, Skv, D, dtype, q_doc, kv_doc=None, *, causal=False, ali
     qd, kd, vd = (inputs.bits_to_f64(x[n], dtype) for n in ("q", "k", "v"))
     od = np.broadcast_to(q_doc, (B, q_doc.shape[1]))
     kdoc = od if kv_doc is None else np.broadcast_to(kv_doc, (B, kv_doc.shape[1]))
-    O, L = oracle.attention(qd, kd, vd, scale=scale, causal=causal, alibi=alibi,
+    O, L = oracle.attention(qd, kd, vd, scale=scale, causal=causal, alibi=alibi, window=window,
                             rowdrop=RD if rowdrop else None, rows=rows, block_mask=block_mask,
                             q_doc=od, kv_doc=kdoc)
     got_o, got_l = to_f64(out), to_f64(lse)
@@ -193,3 +193,30 @@ def test_sparse_negative_and_large_ids(causal):
     remap = np.array([-2 ** 31, -7, 0, 1000, 10 ** 6, 2 ** 30, 2 ** 31 - 1], dtype=np.int64)
     docs = remap[base].astype(np.int32)[None]
     _run(1, 2, 2, 600, 600, 128, "bf16", docs, seed=15, causal=causal)
+
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [40, 300])
+def test_with_sliding_window(window, causal):
+    """Documents AND a window: the key range is the intersection of both, and tiles
+    straddling a document or the band test each pair against both."""
+    docs = inputs.packed_document_ids(16, 2, 700, 5)
+    _run(2, 4, 2, 700, 700, 128, "bf16", docs, seed=16, window=window, causal=causal)
+
+
+def test_with_sliding_window_f16_d64_alibi():
+    docs = inputs.packed_document_ids(17, 1, 513, 4)
+    _run(1, 4, 4, 513, 513, 64, "f16", docs, seed=17, window=64, causal=True, alibi=True)
+
+
+def test_with_sliding_window_and_block_mask():
+    S = 700
+    bm = inputs.random_block_mask(18, (1, 2, -(-S // 128), -(-S // 64)))
+    docs = inputs.packed_document_ids(18, 1, S, 4)
+    _run(1, 2, 2, S, S, 128, "bf16", docs, seed=18, window=100, causal=True, block_mask=bm)
+
+
+def test_with_sliding_window_f32():
+    docs = inputs.packed_document_ids(19, 1, 300, 3)
+    _run(1, 2, 1, 300, 300, 64, "f32", docs, seed=19, window=50)

@@ -185,6 +185,12 @@ def test_integer_scores_document_mask(case):
     _run(x, 128, scale=LN2, exact=True, q_doc=docs, label="doc " + case, **EXACT_CASES[case])
 
 
+def test_integer_scores_document_mask_with_window():
+    x = _integer_inputs(12, 1, 4, 2, 700, 700, 128)
+    docs = inputs.packed_document_ids(12, 1, 700, 5)
+    _run(x, 128, scale=LN2, exact=True, q_doc=docs, causal=True, window=90, label="doc window")
+
+
 def test_integer_scores_document_mask_with_block_mask():
     S = 700
     x = _integer_inputs(10, 1, 4, 4, S, S, 64)
