@@ -276,17 +276,16 @@ void bwd_dq_kernel(BwdParams p) {
         int nxt = cur < nkb ? walk.next(cur + 1, lane, nv) : nkb;
         if (cur < nkb) load_tile(cur, kv0, kv0 + TILEB);
         kv_barrier<0>();
+        // one tile per iteration, the two buffers alternating (a second unrolled copy of
+        // the tile body, as in the dense loop, pushes this variant past 256 VGPRs)
+        int st = 0;
         while (cur < nkb) {
-            tile(cur, cv, kv0, kv0 + TILEB, nxt < nkb ? nxt : -1, kv1, kv1 + TILEB);
+            unsigned char *Kc = st ? kv1 : kv0, *Kn = st ? kv0 : kv1;
+            tile(cur, cv, Kc, Kc + TILEB, nxt < nkb ? nxt : -1, Kn, Kn + TILEB);
             kv_barrier<0>();
             cur = nxt;
             cv = nv;
-            if (cur >= nkb) break;
-            nxt = walk.next(cur + 1, lane, nv);
-            tile(cur, cv, kv1, kv1 + TILEB, nxt < nkb ? nxt : -1, kv0, kv0 + TILEB);
-            kv_barrier<0>();
-            cur = nxt;
-            cv = nv;
+            st ^= 1;
             if (cur < nkb) nxt = walk.next(cur + 1, lane, nv);
         }
     } else {
