@@ -1,7 +1,7 @@
 /*
  * maskmods.h -- C ABI of libmaskmods.so: fused flex-style attention for MI355X (gfx950).
  *
- * Two operations, both asynchronous on the caller's HIP stream:
+ * The operations, all asynchronous on the caller's HIP stream:
  *
  *   mm_attn_fwd     O = softmax(mask_mod(score_mod(scale * Q K^T))) V, plus the
  *                   row log-sum-exp. This is PyTorch's flex_attention operator as the
@@ -12,16 +12,25 @@
  *                   flash-attention kernel", Summary): alibi score_mod, causal and
  *                   sliding-window mask_mods, applied scale first, then score_mod,
  *                   then mask_mod; fully masked rows give O = 0 and LSE = -inf.
+ *                   Beyond those: a row-drop mask_mod, a document mask_mod over
+ *                   captured id tensors, block-sparse masks, fp8 (e4m3) inputs.
+ *
+ *   mm_attn_bwd     the gradients of that forward (dQ, dK, dV) for the same mods,
+ *                   from its O and LSE: the backward the FlyDSL PR lists as a later
+ *                   phase.
  *
  *   mm_attn_decode  one query per head against a KV cache whose length is known
  *                   only at run time, with an optional additive f16 mask: the
  *                   decode attention of IREE issue #19015 ("[ROCM] Support dynamic
  *                   key-value cache sequence length", example IR: Q [B,H,1,D],
  *                   K/V [B,H,?,D], f16 scale, mask [B,H,1,?], f32 score region),
- *                   extended to per-sequence lengths (the issue asks for a dynamic
- *                   batch as well).
+ *                   extended to per-sequence lengths and paged caches (the issue
+ *                   asks for a dynamic batch as well) and to GQA.
  *
- * Conventions shared by both calls
+ *   mm_block_mask_create  the block classes of the built-in predicates, for the
+ *                   block-sparse path of mm_attn_fwd / mm_attn_bwd.
+ *
+ * Conventions shared by the calls
  *   - Tensors are row-major [B, H, S, D] with D innermost (stride 1). Strides are
  *     given in ELEMENTS for the b, h and s dimensions.
  *   - All tensor pointers are DEVICE pointers owned by the caller and borrowed for
@@ -197,7 +206,13 @@ typedef struct mm_bwd_args {
     size_t workspace_bytes;
 } mm_bwd_args;
 
-/* Forward attention. Returns MM_OK or a negative mm_status. */
+/* Forward attention. Returns MM_OK, or (launching nothing) MM_ERR_NULL for a missing
+ * required pointer (q/out when B*Hq*Sq > 0, k/v when B*Hkv*Skv > 0, the document ids),
+ * MM_ERR_DTYPE, MM_ERR_SHAPE (negative sizes, Hq % Hkv, window < 0, non-finite scale or
+ * descales), MM_ERR_UNSUPPORTED (D, unknown score_mod or mask flag), MM_ERR_STRIDE
+ * (negative strides, misaligned bases, strides that are not multiples of the vector
+ * width, tiles whose byte offsets exceed 32 bits); MM_ERR_LAUNCH if the runtime reports
+ * a launch failure. One launch on `stream`. */
 mm_status mm_attn_fwd(const mm_fwd_args *args, void *stream);
 
 /* Bytes of device workspace mm_attn_bwd needs (0 if invalid). */
@@ -211,7 +226,9 @@ size_t mm_attn_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Sq);
  * P = exp(s - LSE), dV = P^T dO, dS = P (dO V^T - rowsum(dO * O)), dQ = scale dS K,
  * dK = scale dS^T Q. P and dS are rounded to the input dtype for their products;
  * accumulation is fp32. Three launches on `stream` (a pre-pass into the workspace,
- * then dQ, then dK/dV); dq, dk, dv are written, not accumulated into. */
+ * then dQ, then dK/dV); dq, dk, dv are written, not accumulated into. bf16/f16 only
+ * (MM_ERR_DTYPE otherwise); a missing or short workspace gives MM_ERR_WORKSPACE; the
+ * other checks are the forward's. */
 mm_status mm_attn_bwd(const mm_bwd_args *args, void *stream);
 
 /* Bytes of device workspace mm_attn_decode needs for these sizes (0 if invalid).
@@ -221,7 +238,9 @@ size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t
 
 /* Decode attention (two launches on `stream`: split pass, then merge). With GQA
  * (Hq > Hkv) one workgroup of the split pass serves up to 8 query heads of a kv head,
- * so K/V are streamed once per kv head. */
+ * so K/V are streamed once per kv head. Rejections as for the forward, plus
+ * MM_ERR_SHAPE for kv_len > Scap or a bad page size, MM_ERR_UNSUPPORTED for a split
+ * count outside 0..256 and MM_ERR_WORKSPACE for a missing or short workspace. */
 mm_status mm_attn_decode(const mm_decode_args *args, void *stream);
 
 /* Split count mm_attn_decode uses when num_splits == 0. */
@@ -235,7 +254,8 @@ int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t k
  * With no flag every block is 2. The table does not depend on b or h: pass it to
  * mm_attn_fwd with block_mask_strides {0, 0, ld} and the same mask_flags, and the
  * result equals that of the predicates alone, with empty blocks never read.
- * MM_MASK_ROWDROP is rejected here (it is per row; mm_attn_fwd applies it anyway).
+ * MM_MASK_ROWDROP and MM_MASK_DOCUMENT are rejected here (MM_ERR_UNSUPPORTED: the
+ * first is per row, the second depends on the ids; mm_attn_fwd applies both anyway).
  * One launch on `stream`; Sq or Skv of 0 writes nothing. */
 mm_status mm_block_mask_create(uint32_t mask_flags, int32_t window, int32_t Sq, int32_t Skv,
                                uint8_t *out, int64_t ld, void *stream);
