@@ -517,6 +517,15 @@ void bwd_dkdv_kernel(BwdParams p) {
                 sacc[rb] = mfma32x32x16(as_vec<V8>(qa), kf[ks], sacc[rb]);
                 dpacc[rb] = mfma32x32x16(as_vec<V8>(da), vf[ks], dpacc[rb]);
             }
+        // operand reads two k-steps ahead of their MFMAs (with one wave per SIMD
+        // nothing else hides an LDS latency); the first group also takes the rows'
+        // lse2 and D reads above (8 per 32-row block)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 * RB + 4 * RB, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
+            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2 * RB, 0);
+        }
         float slope2 = 0.f;
         if (ALIBI) slope2 = (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e;
         uint32_t pp[RB][8], dsp[RB][8];
@@ -569,6 +578,13 @@ void bwd_dkdv_kernel(BwdParams p) {
                 dvacc[db] = mfma32x32x16(pa, as_vec<V8>(u32x4{d0[0], d0[1], d1[0], d1[1]}), dvacc[db]);
                 dkacc[db] = mfma32x32x16(sa, as_vec<V8>(u32x4{q0[0], q0[1], q1[0], q1[1]}), dkacc[db]);
             }
+        }
+        // the transposed reads of a 16-row step issued one step ahead of its MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 1);
+#pragma unroll
+        for (int ks = 0; ks < BQ / 16; ++ks) {
+            if (ks + 1 < BQ / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 1);
         }
     };
 
