@@ -24,8 +24,10 @@
 //
 // Softmax: scores are kept in base-2 units (t = scale*log2(e)*q.k [+ slope*log2(e)*(j-i)]).
 // The running max is only raised when a tile's max exceeds it by more than 2^8 in
-// probability (lazy rescale): P then stays <= 256, exact in the final O / l. Row sums
-// add the fp32 P values; the PV product takes them rounded to 16 bits.
+// probability (lazy rescale): P then stays <= 256, exact in the final O / l. Tiles with
+// no mask or score_mod skip the max altogether: they exponentiate against the running
+// max and fall back to the max only if a lane's sum of P exceeds 256. Row sums add the
+// fp32 P values; the PV product takes them rounded to 16 bits.
 // Semantics (FlyDSL PR #931, Summary): score_mod sees the scaled score, the mask_mod is
 // applied after it, and rows with no kept key give O = 0, LSE = -inf (the running max
 // is clamped to 0 while it is -inf, and the epilogue guards 1/l).
@@ -79,6 +81,7 @@ void fwd_mfma_kernel(FwdParams p) {
     constexpr int LOADS = TILEB / 1024 / NW;        // DMA instructions per wave per tile
     constexpr int RPI = 1024 / TL::ROWB;            // rows per DMA instruction
     constexpr float kRescale = 8.f;                 // lazy-rescale threshold (log2 units)
+    constexpr float kRescaleSum = 256.f;            // 2^kRescale: bound on a plain tile's lane sum
     typedef typename TT::vec8 V8;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
     static_assert(NST == 2 || NST == 3, "stages");
@@ -331,6 +334,26 @@ void fwd_mfma_kernel(FwdParams p) {
             }
             cc = 1.f;
         } else {
+            // plain tile: exponentiate against the running max as it stands. Each P is
+            // non-negative, so a lane sum of at most 2^8 bounds every P by 2^8, the bound
+            // the max test below keeps; the tile takes the max (and maybe the rescale)
+            // only when some lane's sum is larger or not finite (no max yet: m = -inf
+            // gives +inf exponents).
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    const float x0 = fast_exp2(fmaf(sacc[kb][2 * e2], c2, -m_run));
+                    const float x1 = fast_exp2(fmaf(sacc[kb][2 * e2 + 1], c2, -m_run));
+                    pp[kb][e2] = pack2(x0, x1, TT{});
+                    psum += x0;
+                    psum += x1;
+                }
+            if (!__builtin_amdgcn_ballot_w64(!(psum <= kRescaleSum))) {
+                l_run += psum;
+                return;
+            }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
