@@ -126,6 +126,26 @@ def attention_inputs(seed: int, B: int, Hq: int, Hkv: int, Sq: int, Skv: int, D:
     }
 
 
+def rising_score_inputs(seed: int, B: int, H: int, S: int, D: int, dtype: str,
+                        rise: float = 3.0, wobble: float = 8.0, period: float = 700.0) -> dict:
+    """Q, K, V [B,H,S,D] whose scores at scale 1/sqrt(D) climb along the keys.
+
+    Per (b, h) one random unit vector u; q_i = sqrt(D) u + 0.5 n_i and
+    k_j = c_j u + m_j with c_j = rise * j / 64 + wobble * sin(2 pi j / period) and n, m,
+    V standard normal. The scaled score of (i, j) is then about c_j plus unit-size noise:
+    it gains `rise` per 64 keys on average, with stretches where it falls.
+    """
+    g = rng(seed)
+    u = g.standard_normal(size=(B, H, 1, D))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    j = np.arange(S, dtype=np.float64)
+    c = (rise * j / 64.0 + wobble * np.sin(2.0 * np.pi * j / period)).reshape(1, 1, S, 1)
+    q = np.sqrt(D) * u + 0.5 * g.standard_normal(size=(B, H, S, D))
+    k = c * u + g.standard_normal(size=(B, H, S, D))
+    v = g.standard_normal(size=(B, H, S, D))
+    return {n: f32_to_bits(a.astype(np.float32), dtype) for n, a in (("q", q), ("k", k), ("v", v))} | {"dtype": dtype}
+
+
 def pad_lengths(g: np.random.Generator, B: int, L: int) -> np.ndarray:
     """One trailing-pad length per sequence, uniform on {0, ..., L-1}."""
     return g.integers(0, L, size=B, dtype=np.int64)

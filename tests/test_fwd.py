@@ -19,13 +19,14 @@ RD_SEED = 20240
 
 
 def _run(B, Hq, Hkv, Sq, Skv, D, dtype, *, causal=False, mask_causal=False, window=None,
-         alibi=False, rowdrop=False, seed=0, rows=None, scale=None, slopes=None):
+         alibi=False, rowdrop=False, seed=0, rows=None, scale=None, slopes=None, x=None):
     import torch
     import mask_mods_amd as mm
     print(f"[fwd] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal} "
           f"mask_causal={mask_causal} window={window} alibi={alibi} rowdrop={rowdrop} seed={seed}",
           flush=True)
-    x = inputs.attention_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
+    if x is None:
+        x = inputs.attention_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
     q, k, v = (to_torch(x[n], dtype) for n in ("q", "k", "v"))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -173,6 +174,18 @@ def test_causal_flag_equals_causal_mask_mod_and_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("dtype,D,causal", [("bf16", 128, False), ("bf16", 128, True),
+                                             ("f16", 64, False), ("f16", 128, True)])
+def test_scores_rising_along_keys(dtype, D, causal):
+    """Scores that gain about 3 per 64-key tile on average (with stretches where they
+    fall) keep overtaking the running max, so tiles without a mask keep leaving the
+    exponent-first fast path for the max and the rescale; ragged length 1100."""
+    S = 1100
+    print(f"[fwd rising] {dtype} D={D} causal={causal} S={S}", flush=True)
+    x = inputs.rising_score_inputs(31, 1, 2, S, D, dtype)
+    _run(1, 2, 2, S, S, D, dtype, causal=causal, x=x)
 
 
 def test_large_window_equals_no_mask():
