@@ -314,24 +314,35 @@ void fwd_mfma_kernel(FwdParams p) {
             // the lane's document's keys in this tile, [dfirst, dend) as tile offsets
             int dfirst = 0, dend = BN;
             if ((MASK & MASK_DOC) && doc_mask) tile_doc_range(tdoc, mydoc, dfirst, dend);
+            // with alibi, one copy with the predicates and one without, chosen per tile:
+            // inlined separately, so the unmasked copy (alibi tiles off the diagonal)
+            // carries no per-score compare and select. Without alibi a general tile
+            // nearly always needs the predicates (and they keep every pair of a tile
+            // that does not), so only the masked copy is emitted.
+            auto scores = [&](bool masked) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
-                    float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
-                    if (need_mask) {
-                        const int j = k0 + 4 * hi + jo;
-                        bool keep = j < p.Skv;
-                        if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
-                        if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                        if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
-                        t = keep ? t : -INFINITY;
+                    for (int e = 0; e < 16; ++e) {
+                        const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
+                        float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
+                        if (masked) {
+                            const int j = k0 + 4 * hi + jo;
+                            bool keep = j < p.Skv;
+                            if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
+                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                            if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
+                            t = keep ? t : -INFINITY;
+                        }
+                        sacc[kb][e] = t;
+                        mloc = fmaxf(mloc, t);
                     }
-                    sacc[kb][e] = t;
-                    mloc = fmaxf(mloc, t);
                 }
-            }
+            };
+            if (ALIBI && !need_mask)
+                scores(false);
+            else
+                scores(true);
             cc = 1.f;
         } else {
             // plain tile: exponentiate against the running max as it stands. Each P is
