@@ -225,7 +225,9 @@ void bwd_dq_kernel(BwdParams p) {
             }
             // P = 2^(t - lse2) and dS = P (dP - D) as 16-bit pairs, keys in accumulator order
             uint32_t dsp[8];
-            auto make_ds = [&](bool gen) {
+            // gen: scale and alibi applied to the score; masked: the predicates too (an
+            // alibi tile that needs no mask takes gen without masked)
+            auto make_ds = [&](bool gen, bool masked) {
                 const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
 #pragma unroll
                 for (int e2 = 0; e2 < 8; ++e2) {
@@ -237,11 +239,14 @@ void bwd_dq_kernel(BwdParams p) {
                         float pv;
                         if (gen) {
                             const float t = ALIBI ? fmaf(sacc[e], c2, fmaf(slope2, (float)jo, base)) : sacc[e] * c2;
-                            const int j = k0 + 4 * hi + jo;
-                            bool keep = j < p.Skv;
-                            if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
-                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                            if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
+                            bool keep = true;
+                            if (masked) {
+                                const int j = k0 + 4 * hi + jo;
+                                keep = j < p.Skv;
+                                if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
+                                if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
+                                if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
+                            }
                             pv = keep ? fast_exp2(t - lse2) : 0.f;
                         } else {
                             pv = fast_exp2(fmaf(sacc[e], c2, -lse2));
@@ -251,8 +256,12 @@ void bwd_dq_kernel(BwdParams p) {
                     dsp[e2] = pack2(x[0], x[1], TT{});
                 }
             };
-            if (general) make_ds(true);
-            else make_ds(false);
+            if (ALIBI && !need_mask)
+                make_ds(true, false);
+            else if (general)
+                make_ds(true, true);
+            else
+                make_ds(false, false);
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int ks = 2 * kb + half, o4 = 4 * half;
@@ -529,7 +538,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         float slope2 = 0.f;
         if (ALIBI) slope2 = (p.slopes ? p.slopes[h] : exp2f(-8.f * (float)(h + 1) / (float)p.Hq)) * kLog2e;
         uint32_t pp[RB][8], dsp[RB][8];
-        auto make = [&](bool general) {
+        // general: scale and alibi applied to the score; masked: the predicates too
+        auto make = [&](bool general, bool masked) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -543,10 +553,13 @@ void bwd_dkdv_kernel(BwdParams p) {
                         if (general) {
                             const int i = i0 + 32 * rb + 4 * hi + 8 * (e >> 2) + (e & 3);
                             const float t = ALIBI ? fmaf(sacc[rb][e], c2, slope2 * (float)(key - i)) : sacc[rb][e] * c2;
-                            bool keep = key_ok && i < p.Sq;
-                            if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
-                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
-                            if ((MASK & MASK_DOC) && pred) keep &= i - i0 >= dfirst && i - i0 < dend;
+                            bool keep = true;
+                            if (masked) {
+                                keep = key_ok && i < p.Sq;
+                                if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
+                                if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
+                                if ((MASK & MASK_DOC) && pred) keep &= i - i0 >= dfirst && i - i0 < dend;
+                            }
                             x = keep ? fast_exp2(t - lse2) : 0.f;
                             ds[u] = keep ? x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]) : 0.f;
                         } else {
@@ -559,8 +572,12 @@ void bwd_dkdv_kernel(BwdParams p) {
                     dsp[rb][e2] = pack2(ds[0], ds[1], TT{});
                 }
         };
-        if (ALIBI || need_mask) make(true);
-        else make(false);
+        if (need_mask)
+            make(true, true);
+        else if (ALIBI)
+            make(true, false);
+        else
+            make(false, false);
         // dV += P^T dO and dK += dS^T Q over the tile's 16-row k-steps
 #pragma unroll
         for (int ks = 0; ks < BQ / 16; ++ks) {
