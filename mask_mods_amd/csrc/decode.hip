@@ -95,15 +95,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     const uint16_t *kbase = (const uint16_t *)p.k + (PAGED ? 0 : b * p.kv_sb) + hk * p.kv_sh + 8 * c;
     const uint16_t *vbase = (const uint16_t *)p.v + (PAGED ? 0 : b * p.kv_sb) + hk * p.kv_sh + 8 * c;
     const int32_t *bt = PAGED ? p.block_table + b * p.bt_sb : nullptr;
-    // the key this lane loads in step u of the iteration at `base` (tail lanes re-read
-    // the last valid key)
-    auto key_at = [&](int base, int u) { return min(base + u * STEP + slot, j_end - 1); };
-    // page tables: the pages of an iteration's keys are read one iteration ahead, so
-    // the K/V loads never wait on a table read
+    // page tables: the pages of an iteration's keys (the same keys as the loads below)
+    // are read one iteration ahead, so the K/V loads never wait on a table read
     int32_t pg[U];
     if (PAGED && j_begin < j_end) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) pg[u] = bt[key_at(j_begin, u) >> p.page_shift];
+        for (int u = 0; u < U; ++u) pg[u] = bt[min(j_begin + u * STEP + slot, j_end - 1) >> p.page_shift];
     }
 
     float m[G], l[G];
@@ -120,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
         uint16_t mk[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int j = key_at(base, u);
+            const int j = min(base + u * STEP + slot, j_end - 1);  // tail lanes re-read a valid key
             const int64_t off = PAGED ? (int64_t)pg[u] * p.kv_sb + (int64_t)(j & ((1 << p.page_shift) - 1)) * p.kv_ss
                                       : (int64_t)j * p.kv_ss;
             kr[u] = __builtin_nontemporal_load((const u32x4 *)(kbase + off));
@@ -132,7 +129,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
         }
         if (PAGED && base + STEP * U < j_end) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) pg[u] = bt[key_at(base + STEP * U, u) >> p.page_shift];
+            for (int u = 0; u < U; ++u) pg[u] = bt[min(base + STEP * U + u * STEP + slot, j_end - 1) >> p.page_shift];
         }
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
