@@ -237,13 +237,20 @@ size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t
                                      int32_t num_splits);
 
 /* Decode attention (two launches on `stream`: split pass, then merge). With GQA
- * (Hq > Hkv) one workgroup of the split pass serves up to 8 query heads of a kv head,
- * so K/V are streamed once per kv head. Rejections as for the forward, plus
- * MM_ERR_SHAPE for kv_len > Scap or a bad page size, MM_ERR_UNSUPPORTED for a split
- * count outside 0..256 and MM_ERR_WORKSPACE for a missing or short workspace. */
+ * (Hq > Hkv) one workgroup of the split pass serves up to 4 query heads of a kv head,
+ * so K/V are streamed once per 4 query heads (larger groups take several workgroups,
+ * which the automatic split count places on one XCD so that they share its L2).
+ * Rejections as for the forward, plus MM_ERR_SHAPE for kv_len > Scap or a bad page
+ * size, MM_ERR_UNSUPPORTED for a split count outside 0..256 and MM_ERR_WORKSPACE for
+ * a missing or short workspace. */
 mm_status mm_attn_decode(const mm_decode_args *args, void *stream);
 
-/* Split count mm_attn_decode uses when num_splits == 0. */
+/* Split count mm_attn_decode uses when num_splits == 0: about one resident round of
+ * split workgroups (1024 with one query head per workgroup, 512 with 2 or 4), at least
+ * 256 keys per split, at most 256 splits, a multiple of 8 (when 8 or more) if a kv
+ * head's group spans several workgroups. Each split's key range is rounded up to a
+ * whole number of the split loop's iterations, so the last splits of a row may be
+ * empty (they contribute nothing; the workspace size does not change). */
 int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len);
 
 /* Block-mask classes of the built-in mask_mods, the analogue of building a BlockMask

@@ -41,24 +41,34 @@ mm_status check_doc(const mm_mods &m, bool pairs) {
     return MM_OK;
 }
 
-// query heads per split workgroup: the largest of 8, 4, 2, 1 dividing the GQA group
+// Query heads per split workgroup: the largest of 4, 2, 1 that divides the group (a
+// workgroup of 8 heads held too few loads in flight and ran slower than two of 4).
 int decode_heads_per_wg(int32_t Hq, int32_t Hkv) {
     const int group = Hq / Hkv;
-    for (int g = 8; g > 1; g >>= 1)
+    for (int g = 4; g > 1; g >>= 1)
         if (group % g == 0) return g;
     return 1;
 }
 
-// splits: enough (split, head group, batch) workgroups for about one resident round
+// splits: at most one resident round of (split, head group, batch) workgroups, rounded
+// down so that no CU gets one workgroup more than the others: about 1024 with one head
+// per workgroup, 512 with 2 or 4 (their registers leave room for 3 per CU, not 4); no
+// split shorter than kMinKeysPerSplit keys; and, when a kv head's group spans several
+// workgroups, a multiple of 8: workgroups are placed on the 8 XCDs round-robin by
+// linear id (split fastest), so the workgroups that read the same K/V chunk then share
+// one XCD's L2 instead of each fetching it from HBM
 int decode_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t requested) {
     if (requested > 0) return requested;
     if (kv_len <= 0) return 1;
-    const int64_t rows = (int64_t)B * Hq / decode_heads_per_wg(Hq, Hkv);
-    int64_t want = (kTargetDecodeBlocks + rows - 1) / rows;
+    const int G = decode_heads_per_wg(Hq, Hkv);
+    const int64_t rows = (int64_t)B * Hq / G;
+    const int64_t target = G > 1 ? kTargetDecodeBlocks / 2 : kTargetDecodeBlocks;
+    int64_t want = target / rows;
     const int64_t by_len = ((int64_t)kv_len + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
     if (want > by_len) want = by_len;
-    if (want < 1) want = 1;
     if (want > kMaxSplits) want = kMaxSplits;
+    if (Hq / Hkv > G && want >= 8) want = want / 8 * 8;
+    if (want < 1) want = 1;
     return (int)want;
 }
 
@@ -349,6 +359,12 @@ mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
     p.group = a->Hq / a->Hkv;
     p.splits = splits;
     p.chunk = a->kv_len > 0 ? (a->kv_len + splits - 1) / splits : 1;
+    {
+        // whole loop iterations per split (the last splits may then be empty)
+        const int64_t it = decode_iter_keys(a->D, decode_heads_per_wg(a->Hq, a->Hkv));
+        const int64_t aligned = (p.chunk + it - 1) / it * it;
+        if (aligned * splits <= INT32_MAX) p.chunk = (int)aligned;
+    }
     p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1];
     p.kv_sb = a->kv_strides[0]; p.kv_sh = a->kv_strides[1]; p.kv_ss = a->kv_strides[2];
     p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1];

@@ -14,8 +14,9 @@
 //   pass 2 (merge): per (b, h) rescale the partials to the common max and normalise:
 //     O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, LSE = (M + log2 L) ln 2.
 // A row with no visible key (empty sequence or all -inf mask) yields O = 0, LSE = -inf.
-// With GQA a workgroup serves all (up to 8) query heads of a kv head, so each K/V byte
-// is read once; with a page table the K/V rows are gathered page by page.
+// With GQA a workgroup serves up to 4 query heads of a kv head (all of a group of 2 or
+// 4), so each K/V byte is read once per 4 heads; with a page table the K/V rows are
+// gathered page by page.
 #include "common.h"
 #include "kernels.h"
 
@@ -67,8 +68,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     constexpr int KPW = 64 / LPK;    // keys per wave per step
     constexpr int NW = 4;
     constexpr int STEP = NW * KPW;   // keys per workgroup per step
-    constexpr int U = G <= 2 ? 8 : (G == 4 ? 4 : 2);  // steps in flight per iteration
+    constexpr int U = decode_steps_in_flight(G);  // steps in flight per iteration
     constexpr int SLOTS = NW * KPW;  // partial softmax states per workgroup and head
+    static_assert(STEP * U == decode_iter_keys(D, G), "iteration size shared with the host");
+    static_assert(G == 1 || G == 2 || G == 4, "heads per workgroup");
 
     __shared__ float sm_m[SLOTS], sm_l[SLOTS];
     __shared__ __attribute__((aligned(16))) float sm_o[SLOTS][D];
@@ -260,7 +263,6 @@ static hipError_t launch_decode_t(const DecParams &p, hipStream_t s) {
     hipError_t e;
     const bool paged = p.block_table != nullptr;
     switch (p.heads_per_wg) {
-        case 8: e = paged ? launch_split<TT, D, 8, true>(p, s) : launch_split<TT, D, 8, false>(p, s); break;
         case 4: e = paged ? launch_split<TT, D, 4, true>(p, s) : launch_split<TT, D, 4, false>(p, s); break;
         case 2: e = paged ? launch_split<TT, D, 2, true>(p, s) : launch_split<TT, D, 2, false>(p, s); break;
         default: e = paged ? launch_split<TT, D, 1, true>(p, s) : launch_split<TT, D, 1, false>(p, s); break;

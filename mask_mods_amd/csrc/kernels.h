@@ -72,11 +72,18 @@ struct DecParams {
     float *ws_o;           // [B, Hq, splits, D] unnormalised partial outputs
     float *ws_m;           // [B, Hq, splits] partial row max (base 2)
     float *ws_l;           // [B, Hq, splits] partial row sum
-    int heads_per_wg;      // query heads per split workgroup (1, 2, 4 or 8; divides group)
+    int heads_per_wg;      // query heads per split workgroup (1, 2 or 4; divides group)
     const int32_t *block_table;  // paged caches: [B, max_pages] page ids, or nullptr
     int64_t bt_sb;         // block-table row stride (elements)
     int page_shift;        // log2(page_size)
 };
+
+// Decode split pass: steps of keys in flight per loop iteration (8 with up to 2 query
+// heads per workgroup, 4 with 4: the registers hold G queries and outputs), and the
+// keys one iteration of a workgroup covers (4 waves, D/8 lanes per key). The host makes
+// split chunks whole multiples of it, so no iteration runs partly empty.
+constexpr int decode_steps_in_flight(int G) { return G <= 2 ? 8 : 4; }
+constexpr int decode_iter_keys(int D, int G) { return 4 * (64 / (D / 8)) * decode_steps_in_flight(G); }
 
 // Smallest number of query rows per forward workgroup (host-side grid bound).
 constexpr int kFwdBM = 128;

@@ -177,13 +177,16 @@ def test_fp8_args_rejected_before_launch(kw, status):
 
 
 def test_decode_splits_count_head_groups():
-    """With GQA a split workgroup serves up to 8 query heads, so the automatic split
-    count targets the same number of workgroups with G times more splits."""
-    assert mm.decode_auto_splits(1, 32, 32768, Hkv=8) == 128      # group 4: 8 head groups
-    assert mm.decode_auto_splits(1, 32, 32768, Hkv=4) == 128      # group 8: 4 head groups, len bound
-    assert mm.decode_auto_splits(1, 32, 32768, Hkv=32) == 32
-    assert mm.decode_auto_splits(2, 24, 8192, Hkv=8) == 22        # group 3: one head per workgroup, ceil(1024/48)
-    assert mm.decode_workspace_size(1, 32, 32768, 128, Hkv=8) == 32 * 128 * 130 * 4
+    """With GQA a split workgroup serves up to 4 query heads. The automatic split count
+    aims at 1024 workgroups with one head per workgroup and 512 with 2 or 4, rounding
+    down; when a kv head's group spans several workgroups it is a multiple of 8."""
+    assert mm.decode_auto_splits(1, 32, 32768, Hkv=8) == 64       # group 4: 8 head groups, 512 / 8
+    assert mm.decode_auto_splits(1, 32, 32768, Hkv=4) == 64       # group 8: two workgroups of 4 per kv head
+    assert mm.decode_auto_splits(1, 32, 32768, Hkv=16) == 32      # group 2: 16 head groups, 512 / 16
+    assert mm.decode_auto_splits(1, 32, 32768, Hkv=32) == 32      # one head per workgroup, 1024 / 32
+    assert mm.decode_auto_splits(2, 24, 8192, Hkv=8) == 16        # group 3: one head each, 1024 // 48 = 21 -> 16
+    assert mm.decode_auto_splits(8, 32, 32768, Hkv=32) == 4
+    assert mm.decode_workspace_size(1, 32, 32768, 128, Hkv=8) == 32 * 64 * 130 * 4
     assert mm.load_library().mm_attn_decode_auto_splits(1, 32, 5, 100) == 0  # Hq % Hkv != 0
 
 

@@ -153,10 +153,10 @@ def test_workspace_reuse_across_calls_and_split_counts():
 
 
 # ------------------------------------------------------------ GQA head groups
-@pytest.mark.parametrize("Hq,Hkv", [(32, 16), (32, 8), (32, 4), (24, 8), (64, 4)])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 16), (32, 8), (32, 4), (24, 8), (48, 8), (64, 4)])
 def test_gqa_head_groups(Hq, Hkv):
-    """Group sizes 2, 4, 8 (one workgroup per group), 3 (one head per workgroup) and 16
-    (two workgroups of 8 heads per kv head)."""
+    """Group sizes 2 and 4 (one workgroup per group), 8 and 16 (two and four workgroups
+    of 4 heads per kv head), 3 (one head per workgroup) and 6 (three workgroups of 2)."""
     _run(2, Hq, Hkv, [2500, 777], 128, "f16", bias_seed=13, seed=13)
 
 
@@ -211,6 +211,11 @@ def test_paged(page_size):
 
 def test_paged_gqa_no_mask_forced_splits():
     _paged_run(2, 32, 8, [4096, 333], 128, "bf16", 64, seed=16, use_mask=False, num_splits=7)
+
+
+def test_paged_gqa_group_8():
+    """Two workgroups of 4 query heads per kv head, each gathering the same pages."""
+    _paged_run(2, 32, 4, [5000, 2049], 128, "f16", 16, seed=18)
 
 
 def test_paged_long_and_empty():
