@@ -190,6 +190,23 @@ def test_decode_splits_count_head_groups():
     assert mm.load_library().mm_attn_decode_auto_splits(1, 32, 5, 100) == 0  # Hq % Hkv != 0
 
 
+def test_decode_auto_splits_properties():
+    """Over many shapes: at most one round of split workgroups (1024 with one head per
+    workgroup, 512 with 2 or 4), never more splits than 256-key chunks or 256, and a
+    multiple of 8 whenever a kv head's group spans several workgroups."""
+    for B in (1, 2, 3, 8, 64):
+        for Hq, Hkv in ((32, 32), (32, 16), (32, 8), (32, 4), (24, 8), (48, 8), (64, 4), (40, 5), (7, 1)):
+            for L in (1, 255, 256, 1000, 8192, 32768, 262144):
+                s = mm.decode_auto_splits(B, Hq, L, Hkv=Hkv)
+                group = Hq // Hkv
+                G = next(g for g in (4, 2, 1) if group % g == 0)
+                assert 1 <= s <= min(256, -(-L // 256)), (B, Hq, Hkv, L, s)
+                if s > 1:
+                    assert (B * Hq // G) * s <= (1024 if G == 1 else 512), (B, Hq, Hkv, L, s)
+                if group > G and s >= 8:
+                    assert s % 8 == 0, (B, Hq, Hkv, L, s)
+
+
 @pytest.mark.parametrize("page_size,stride,status", [(12, 64, SHAPE), (0, 64, SHAPE), (16, -1, STRIDE),
                                                      (16, 2, STRIDE)])
 def test_decode_rejects_bad_page_tables(page_size, stride, status):
