@@ -605,14 +605,53 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
     };
 
-    if (n_it > 0) load_tile(0, qd0);
-    kv_barrier<0>();
-    for (int n = 0; n < n_it; n += 2) {
-        tile(n, qd0, n + 1 < n_it ? n + 1 : -1, qd1);
+    if constexpr ((MASK & MASK_BLOCK) && BNK == kBlockKV) {
+        // The workgroup's keys are one block column of the block mask, so an item's
+        // class is the same for all its waves: items whose block is empty are skipped
+        // outright (no copy, no barrier). Their classes are read 64 items at a time, a
+        // byte per lane, and walked by ballot; every wave derives the same sequence.
+        int wbase = -64, wv = 0;
+        uint64_t wm = 0;
+        auto next_item = [&](int from) -> int {
+            while (from < n_it) {
+                if (from >= wbase + 64) {
+                    wbase = from & ~63;
+                    const int t = wbase + lane;
+                    wv = 0;
+                    if (t < n_it) {
+                        const int h = hk * p.group + t / nq, qt = qt_lo + t % nq;
+                        wv = p.bm[b * p.bm_sb + h * p.bm_sh + (int64_t)(qt * BQ / kBlockQ) * p.bm_sq + kt];
+                    }
+                    wm = __builtin_amdgcn_ballot_w64(wv != 0);
+                }
+                const uint64_t m = wm & (~0ull << (from - wbase));
+                if (m) return wbase + (int)__builtin_ctzll(m);
+                from = wbase + 64;
+            }
+            return n_it;
+        };
+        int cur = next_item(0);
+        if (cur < n_it) load_tile(cur, qd0);
         kv_barrier<0>();
-        if (n + 1 < n_it) {
-            tile(n + 1, qd1, n + 2 < n_it ? n + 2 : -1, qd0);
+        while (cur < n_it) {
+            const int nx = next_item(cur + 1);
+            tile(cur, qd0, nx < n_it ? nx : -1, qd1);
             kv_barrier<0>();
+            if (nx >= n_it) break;
+            cur = next_item(nx + 1);
+            tile(nx, qd1, cur < n_it ? cur : -1, qd0);
+            kv_barrier<0>();
+        }
+    } else {
+        if (n_it > 0) load_tile(0, qd0);
+        kv_barrier<0>();
+        for (int n = 0; n < n_it; n += 2) {
+            tile(n, qd0, n + 1 < n_it ? n + 1 : -1, qd1);
+            kv_barrier<0>();
+            if (n + 1 < n_it) {
+                tile(n + 1, qd1, n + 2 < n_it ? n + 2 : -1, qd0);
+                kv_barrier<0>();
+            }
         }
     }
 
@@ -633,7 +672,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 template <typename TT, int D, bool A, int M>
 hipError_t launch_bwd_one(BwdParams p, hipStream_t s) {
-    constexpr int NW = 4;
+    // dK/dV workgroup: 4 waves (128 keys); with a block mask 2 waves, so that its 64
+    // keys are one block column and empty blocks skip whole items
+    constexpr int NW = (M & MASK_BLOCK) ? 2 : 4;
     // dQ workgroup: 8 waves (256 rows share each K/V tile) without a mask or with
     // causal alone, as in the forward (each 1-1.5% faster overall at S = 8192); other
     // masks keep 128-row tiles

@@ -110,6 +110,32 @@ def test_block_mask(pred):
     _check(1, 4, 2, S, S, 128, "bf16", seed=6, block_mask=bm, **({"causal": True} if pred == "causal" else {}))
 
 
+def test_block_mask_sparse_gqa_ragged():
+    """A mostly empty table (90% of blocks empty) with GQA group 4 and ragged lengths:
+    a dK/dV workgroup visits only its non-empty (query head, query tile) items, and with
+    4 heads x 18 query tiles per key block it walks more than one 64-item window."""
+    Sq, Skv = 1100, 1060
+    bm = inputs.random_block_mask(41, (1, 8, -(-Sq // 128), -(-Skv // 64)), p_empty=0.9, p_full=0.05)
+    _check(1, 8, 2, Sq, Skv, 64, "bf16", seed=41, block_mask=bm)
+
+
+def test_block_mask_per_batch_broadcast_over_heads():
+    """A table per batch, broadcast over heads (head stride 0), with causal."""
+    S = 500
+    bm = inputs.random_block_mask(42, (2, 1, -(-S // 128), -(-S // 64)), p_empty=0.5, p_full=0.25)
+    _check(2, 4, 2, S, S, 128, "bf16", seed=42, causal=True, block_mask=bm)
+
+
+def test_block_mask_all_empty():
+    """Every block empty: no item is visited, every gradient is zero."""
+    import torch
+    S = 300
+    bm = np.zeros((1, 1, -(-S // 128), -(-S // 64)), dtype=np.uint8)
+    dq, dk, dv = _check(1, 4, 2, S, S, 64, "bf16", seed=43, block_mask=bm)
+    for t in (dq, dk, dv):
+        assert torch.count_nonzero(t).item() == 0
+
+
 def test_created_causal_classes_match_plain_causal_bitwise():
     import torch
     import mask_mods_amd as mm
