@@ -264,8 +264,9 @@ def main():
     if args.ingest:
         return ingest(args.ingest)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the attention shards by (batch, head) with no exchange; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(attention shards by (batch, head) with no exchange between GPUs, so each "
+              "GPU would run the same kernels on its own share).",
               file=sys.stderr)
         sys.exit(2)
 
