@@ -278,6 +278,11 @@ size_t mm_bwd_args_size(void);
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t mm_version(void);
 
+/* Identifier of the sources this library was compiled from (a hash of the kernel, ABI
+ * and header files, "unknown" if the build did not set it). A binding can compare it
+ * with the sources it ships to refuse a stale library. Static string, never freed. */
+const char *mm_source_hash(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # MASKMODS_LIB may point at another build of the library (e.g. a tuning variant)
-_LIB_PATH = os.environ.get("MASKMODS_LIB") or os.path.join(_PKG, "libmaskmods.so")
+_DEFAULT_LIB = os.path.join(_PKG, "libmaskmods.so")
+_LIB_PATH = os.environ.get("MASKMODS_LIB") or _DEFAULT_LIB
 
 MM_F32, MM_F16, MM_BF16, MM_FP8_E4M3 = 0, 1, 2, 3
 SCORE_NONE, SCORE_ALIBI = 0, 1
@@ -160,6 +161,16 @@ def load_library():
     lib.mm_fwd_args_size.restype = ctypes.c_size_t
     lib.mm_decode_args_size.restype = ctypes.c_size_t
     lib.mm_version.restype = ctypes.c_int32
+    lib.mm_source_hash.restype = ctypes.c_char_p
+    if _LIB_PATH == _DEFAULT_LIB:
+        # the in-tree library must come from the sources beside it: a stale build would
+        # run kernels and a workspace contract this binding does not describe
+        from .build import source_hash
+        built, here = lib.mm_source_hash().decode(), source_hash()
+        if built != here:
+            raise RuntimeError(
+                f"{_LIB_PATH} was built from other sources (library {built}, sources {here}); "
+                "run `python -m mask_mods_amd.build` (or __graft_entry__.build()) again")
     if lib.mm_fwd_args_size() != ctypes.sizeof(FwdArgs):
         raise RuntimeError("mm_fwd_args layout mismatch between library and binding")
     if lib.mm_decode_args_size() != ctypes.sizeof(DecodeArgs):

@@ -6,6 +6,7 @@ written atomically to ``mask_mods_amd/libmaskmods.so``.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -46,6 +47,21 @@ SOURCES = [
 ]
 
 
+def source_hash() -> str:
+    """Hash of every kernel, ABI and header source the library is built from (16 hex
+    digits). The build stamps it into the library; the binding compares the two at load,
+    so a library left over from other sources is refused instead of run."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            if os.path.splitext(name)[1] in (".hip", ".h", ".cpp"):
+                h.update(name.encode() + b"\0")
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+                h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
 def _compile(src: str, extra, build_dir: str = BUILD) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
@@ -64,6 +80,7 @@ def build(jobs: int | None = None, resource_usage: bool = False, defines=(), out
     os.makedirs(build_dir, exist_ok=True)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
     extra += [f"-D{d}" for d in defines]
+    extra += [f"-DMM_SOURCE_HASH=\"{source_hash()}\""]
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))

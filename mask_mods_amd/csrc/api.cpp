@@ -78,6 +78,11 @@ extern "C" {
 
 int32_t mm_version(void) { return 400; }
 
+#ifndef MM_SOURCE_HASH
+#define MM_SOURCE_HASH "unknown"
+#endif
+const char *mm_source_hash(void) { return MM_SOURCE_HASH; }
+
 size_t mm_fwd_args_size(void) { return sizeof(mm_fwd_args); }
 size_t mm_decode_args_size(void) { return sizeof(mm_decode_args); }
 size_t mm_bwd_args_size(void) { return sizeof(mm_bwd_args); }

@@ -38,6 +38,16 @@ def test_struct_layouts_match():
     assert lib.mm_version() >= 400
 
 
+def test_library_built_from_these_sources():
+    """The in-tree library carries the hash of the sources beside it (the binding refuses
+    a mismatch at load, so a stale build cannot run)."""
+    from mask_mods_amd.build import source_hash
+    lib = mm.load_library()
+    if mm.library_path() == mm._DEFAULT_LIB:
+        assert lib.mm_source_hash().decode() == source_hash()
+    assert len(source_hash()) == 16
+
+
 def test_status_strings():
     lib = mm.load_library()
     for st in (OK, NULL, SHAPE, DTYPE, UNSUP, STRIDE, LAUNCH, WORKSPACE):
