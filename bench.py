@@ -400,6 +400,40 @@ def main():
             ent["latency_vs_no_mod"] = round(t / fwd_avg_s, 3)
             cases[name] = ent
 
+    # ---- GQA cross-attention at its own shape: B2 Hq32 Hkv8 D128 Sq1024 Skv8192, bf16 and
+    # f16, with the hash mask_mod that drops about 5% of the query rows, then also
+    # WINDOW(256) AND causal on raw (top-left) indices. Kept pairs are counted from the
+    # kernel's own LSE: a dropped row is the only kind with LSE = -inf here.
+    gcases = {}
+    if not args.no_cases:
+        Bg, Hqg, Hkvg, Sqg, Skvg, Wg = 2, 32, 8, 1024, 8192, 256
+        rd = (20240, int(0.05 * 2 ** 32))
+        dense_g = fwd_flops(Bg, Hqg, Sqg, Skvg, D)
+        for dt in ("bf16", "f16"):
+            xg = inputs.attention_inputs(4, Bg, Hqg, Hkvg, Sqg, Skvg, D, dt)
+            gq, gk, gv = (dev_tensor(xg[n], dt) for n in ("q", "k", "v"))
+            gout = torch.empty_like(gq)
+            glse = torch.empty(Bg, Hqg, Sqg, dtype=torch.float32, device=dev)
+            for wname, kw in (("rowdrop", {}), ("rowdrop_window", dict(window=Wg, mask_flags=mm.MASK_CAUSAL))):
+                for _ in range(5):
+                    mm.attn_fwd(gq, gk, gv, scale, rowdrop=rd, out=gout, lse=glse, **kw)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = 20
+                e0.record(stream)
+                for _ in range(n):
+                    mm.attn_fwd(gq, gk, gv, scale, rowdrop=rd, out=gout, lse=glse, **kw)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) / n * 1e-3
+                live = torch.isfinite(glse).cpu().numpy()  # [B, Hq, Sq]
+                per_row = (np.full(Sqg, Skvg) if wname == "rowdrop"
+                           else np.minimum(np.arange(Sqg), Wg) + 1)
+                kept = int((live * per_row[None, None, :]).sum())
+                gcases[f"{dt}_{wname}"] = {
+                    "us": round(t * 1e6, 1), "tflops_dense_equiv": round(dense_g / t / 1e12, 1),
+                    "tflops_algorithmic": round(4.0 * D * kept / t / 1e12, 1),
+                    "rows_dropped": round(1.0 - float(live.mean()), 4)}
+
     traffic_fwd = load_traffic(FWD_KERNEL)
     traffic_dec = load_traffic("decode")
     res = {
@@ -433,6 +467,9 @@ def main():
                          "algorithmic": f"{dbytes} bytes per call (K+V+mask+q+out+lse)"},
         },
         "cases_s8192": cases,
+        "cases_gqa_cross": {"workload": "fwd B2 Hq32 Hkv8 D128 Sq1024 Skv8192, ~5% of query rows dropped "
+                                        "by a hash mask_mod; _window adds |i-j|<=256 AND j<=i (top-left)",
+                            **gcases} if gcases else {},
     }
     # decode variants: GQA (Hq 32 / Hkv 8: K/V streamed once per kv head) and a paged
     # cache (B 8, 64-key pages scattered over a pool by a seeded permutation)
