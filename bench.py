@@ -400,6 +400,29 @@ def main():
             ent["latency_vs_no_mod"] = round(t / fwd_avg_s, 3)
             cases[name] = ent
 
+    # ---- the dense workload's shorter lengths: S 2048 and 4096, no mod and causal
+    scases = {}
+    if not args.no_cases:
+        for Ss in (2048, 4096):
+            xs = inputs.attention_inputs(2, B, H, H, Ss, Ss, D, "bf16")
+            sq_, sk_, sv_ = (dev_tensor(xs[n], "bf16") for n in ("q", "k", "v"))
+            sout = torch.empty_like(sq_)
+            slse = torch.empty(B, H, Ss, dtype=torch.float32, device=dev)
+            for cname, causal in (("no_mod", False), ("causal", True)):
+                for _ in range(5):
+                    mm.attn_fwd(sq_, sk_, sv_, scale, causal=causal, out=sout, lse=slse)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = 20
+                e0.record(stream)
+                for _ in range(n):
+                    mm.attn_fwd(sq_, sk_, sv_, scale, causal=causal, out=sout, lse=slse)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) / n * 1e-3
+                alg = fwd_flops(B, H, Ss, Ss, D, causal=causal)
+                scases[f"s{Ss}_{cname}"] = {"us": round(t * 1e6, 1), "tflops_algorithmic": round(alg / t / 1e12, 1),
+                                            "frac_bf16_peak": round(alg / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
     # ---- GQA cross-attention at its own shape: B2 Hq32 Hkv8 D128 Sq1024 Skv8192, bf16 and
     # f16, with the hash mask_mod that drops about 5% of the query rows, then also
     # WINDOW(256) AND causal on raw (top-left) indices. Kept pairs are counted from the
@@ -467,6 +490,8 @@ def main():
                          "algorithmic": f"{dbytes} bytes per call (K+V+mask+q+out+lse)"},
         },
         "cases_s8192": cases,
+        "cases_dense_short": ({"workload": "fwd bf16 B2 H32 D128 Sq=Skv in {2048, 4096} +LSE; causal half-counted",
+                               **scases} if scases else {}),
         "cases_gqa_cross": {"workload": "fwd B2 Hq32 Hkv8 D128 Sq1024 Skv8192, ~5% of query rows dropped "
                                         "by a hash mask_mod; _window adds |i-j|<=256 AND j<=i (top-left)",
                             **gcases} if gcases else {},

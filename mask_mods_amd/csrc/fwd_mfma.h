@@ -550,26 +550,39 @@ void fwd_mfma_kernel(FwdParams p) {
 #define MM_FWD_NW_MASKED 4  // window, document or block masks: finer row tiles skip more keys
 #endif
 #ifndef MM_FWD_NW_CAUSAL
-#define MM_FWD_NW_CAUSAL 8  // causal alone: the shared tiles outweigh the idle diagonal waves
+#define MM_FWD_NW_CAUSAL 8  // causal alone on long rows: the shared tiles outweigh the idle diagonal waves
 #endif
 #ifndef MM_FWD_NST
 #define MM_FWD_NST 2
 #endif
 
-template <typename TT, int D, bool A, int M>
-hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
-    // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic. Causal
-    // alone keeps 8 (1.5% faster at S = 8192 than 4 despite the waves idle past the
-    // diagonal); with a window or documents, 4-wave tiles (128 rows) follow the band
-    // more closely and skip more key tiles, which matters more; a block mask's q-blocks
-    // are 128 rows, one 4-wave workgroup each
-    constexpr int NW = M == 0 ? MM_FWD_NW : (M == MASK_CAUSAL ? MM_FWD_NW_CAUSAL : MM_FWD_NW_MASKED),
-                  NST = MM_FWD_NST;
+#ifndef MM_FWD_CAUSAL_SHORT
+#define MM_FWD_CAUSAL_SHORT 4096  // causal, D = 128: at most this many visible keys -> 4 waves
+#endif
+
+template <typename TT, int D, bool A, int M, int NW>
+hipError_t launch_fwd_mfma_nw(FwdParams p, hipStream_t s) {
+    constexpr int NST = MM_FWD_NST;
     static_assert(!(M & MASK_BLOCK) || NW == 4, "block masks use 128-row workgroups");
     p.n_qtiles = (p.Sq + 32 * NW - 1) / (32 * NW);
     const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(64 * NW);
     fwd_mfma_kernel<TT, D, A, M, NW, NST><<<grid, block, 0, s>>>(p);
     return hipGetLastError();
+}
+
+template <typename TT, int D, bool A, int M>
+hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
+    // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic. Causal
+    // alone keeps 8 on long rows (at S = 8192 as fast as 4 without a score_mod, 3% faster
+    // with alibi) but takes 4 when at most 4096 keys are visible (S 2048 and 4096: 5-6%
+    // faster, 10-15% with alibi: the finer tiles idle less past the diagonal); with a
+    // window or documents, 4-wave tiles (128 rows) follow the band more closely and skip
+    // more key tiles, which matters more; a block mask's q-blocks are 128 rows, one
+    // 4-wave workgroup each
+    constexpr int NW = M == 0 ? MM_FWD_NW : (M == MASK_CAUSAL ? MM_FWD_NW_CAUSAL : MM_FWD_NW_MASKED);
+    if (M == MASK_CAUSAL && D == 128 && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= MM_FWD_CAUSAL_SHORT)
+        return launch_fwd_mfma_nw<TT, D, A, M, 4>(p, s);
+    return launch_fwd_mfma_nw<TT, D, A, M, NW>(p, s);
 }
 
 template <typename TT, int D>
