@@ -573,14 +573,17 @@ hipError_t launch_fwd_mfma_nw(FwdParams p, hipStream_t s) {
 template <typename TT, int D, bool A, int M>
 hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
     // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic. Causal
-    // alone keeps 8 on long rows (at S = 8192 as fast as 4 without a score_mod, 3% faster
-    // with alibi) but takes 4 when at most 4096 keys are visible (S 2048 and 4096: 5-6%
-    // faster, 10-15% with alibi: the finer tiles idle less past the diagonal); with a
-    // window or documents, 4-wave tiles (128 rows) follow the band more closely and skip
-    // more key tiles, which matters more; a block mask's q-blocks are 128 rows, one
-    // 4-wave workgroup each
-    constexpr int NW = M == 0 ? MM_FWD_NW : (M == MASK_CAUSAL ? MM_FWD_NW_CAUSAL : MM_FWD_NW_MASKED);
-    if (M == MASK_CAUSAL && D == 128 && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= MM_FWD_CAUSAL_SHORT)
+    // alone at D = 128 keeps 8 on long rows (at S = 8192 as fast as 4 without a
+    // score_mod, 3% faster with alibi) but takes 4 when at most 4096 keys are visible
+    // (S 2048 and 4096: 5-6% faster, 10-15% with alibi: the finer tiles idle less past
+    // the diagonal); with a window or documents, 4-wave tiles (128 rows) follow the band
+    // more closely and skip more key tiles, which matters more; a block mask's q-blocks
+    // are 128 rows, one 4-wave workgroup each. D = 64 always takes 4: its halved tile
+    // products leave the shared copies less to gain (no mod 7-15% faster at S 2048 to
+    // 8192, causal 6-15%, alibi 0-3%)
+    constexpr int NW = D == 64 ? 4
+                               : (M == 0 ? MM_FWD_NW : (M == MASK_CAUSAL ? MM_FWD_NW_CAUSAL : MM_FWD_NW_MASKED));
+    if (M == MASK_CAUSAL && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= MM_FWD_CAUSAL_SHORT)
         return launch_fwd_mfma_nw<TT, D, A, M, 4>(p, s);
     return launch_fwd_mfma_nw<TT, D, A, M, NW>(p, s);
 }
