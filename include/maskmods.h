@@ -116,7 +116,8 @@ enum {
 typedef struct mm_mods {
     int32_t score_mod;            /* mm_score_mod                                      */
     uint32_t mask_flags;          /* OR of MM_MASK_*                                   */
-    int32_t window;               /* MM_MASK_WINDOW half-width, >= 0                   */
+    int32_t window;               /* MM_MASK_WINDOW half-width, 0..INT32_MAX; any value
+                                     >= max(Sq, Skv) keeps every pair                   */
     uint32_t rowdrop_seed;        /* MM_MASK_ROWDROP                                   */
     uint32_t rowdrop_threshold;   /* MM_MASK_ROWDROP: ~threshold/2^32 of rows dropped  */
     const float *alibi_slopes;    /* device fp32 [Hq], or NULL for 2^(-8(h+1)/Hq)      */
@@ -139,7 +140,7 @@ typedef struct mm_fwd_args {
     float *lse;           /* [B, Hq, Sq] fp32 contiguous, or NULL                     */
     int32_t dtype;        /* mm_dtype: MM_BF16, MM_F16, MM_FP8_E4M3 (MFMA paths) or
                              MM_F32; `out` has this dtype, except bf16 for fp8 inputs   */
-    int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128}                                 */
+    int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128}; Sq, Skv < 2^30                 */
     int64_t q_strides[3]; /* elements, for b, h, s                                    */
     int64_t k_strides[3];
     int64_t v_strides[3];
@@ -196,7 +197,7 @@ typedef struct mm_bwd_args {
     void *dk;                /* [B, Hkv, Skv, D]                                         */
     void *dv;                /* [B, Hkv, Skv, D]                                         */
     int32_t dtype;           /* MM_BF16 or MM_F16                                         */
-    int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128}                                    */
+    int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128}; Sq, Skv < 2^30                    */
     int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3], do_strides[3];
     int64_t dq_strides[3], dk_strides[3], dv_strides[3]; /* elements, for b, h, s        */
     float scale;             /* the forward's scale                                       */
@@ -208,8 +209,8 @@ typedef struct mm_bwd_args {
 
 /* Forward attention. Returns MM_OK, or (launching nothing) MM_ERR_NULL for a missing
  * required pointer (q/out when B*Hq*Sq > 0, k/v when B*Hkv*Skv > 0, the document ids),
- * MM_ERR_DTYPE, MM_ERR_SHAPE (negative sizes, Hq % Hkv, window < 0, non-finite scale or
- * descales), MM_ERR_UNSUPPORTED (D, unknown score_mod or mask flag), MM_ERR_STRIDE
+ * MM_ERR_DTYPE, MM_ERR_SHAPE (negative sizes, Sq or Skv >= 2^30, Hq % Hkv, window < 0,
+ * non-finite scale or descales), MM_ERR_UNSUPPORTED (D, unknown score_mod or mask flag), MM_ERR_STRIDE
  * (negative strides, misaligned bases, strides that are not multiples of the vector
  * width, tiles whose byte offsets exceed 32 bits); MM_ERR_LAUNCH if the runtime reports
  * a launch failure. One launch on `stream`. */

@@ -25,9 +25,7 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# MASKMODS_LIB may point at another build of the library (e.g. a tuning variant)
-_DEFAULT_LIB = os.path.join(_PKG, "libmaskmods.so")
-_LIB_PATH = os.environ.get("MASKMODS_LIB") or _DEFAULT_LIB
+_LIB_PATH = os.path.join(_PKG, "libmaskmods.so")
 
 MM_F32, MM_F16, MM_BF16, MM_FP8_E4M3 = 0, 1, 2, 3
 SCORE_NONE, SCORE_ALIBI = 0, 1
@@ -162,15 +160,14 @@ def load_library():
     lib.mm_decode_args_size.restype = ctypes.c_size_t
     lib.mm_version.restype = ctypes.c_int32
     lib.mm_source_hash.restype = ctypes.c_char_p
-    if _LIB_PATH == _DEFAULT_LIB:
-        # the in-tree library must come from the sources beside it: a stale build would
-        # run kernels and a workspace contract this binding does not describe
-        from .build import source_hash
-        built, here = lib.mm_source_hash().decode(), source_hash()
-        if built != here:
-            raise RuntimeError(
-                f"{_LIB_PATH} was built from other sources (library {built}, sources {here}); "
-                "run `python -m mask_mods_amd.build` (or __graft_entry__.build()) again")
+    # the library must come from the sources beside it: a stale build would run kernels
+    # and a workspace contract this binding does not describe
+    from .build import source_hash
+    built, here = lib.mm_source_hash().decode(), source_hash()
+    if built != here:
+        raise RuntimeError(
+            f"{_LIB_PATH} was built from other sources (library {built}, sources {here}); "
+            "run `python -m mask_mods_amd.build` (or __graft_entry__.build()) again")
     if lib.mm_fwd_args_size() != ctypes.sizeof(FwdArgs):
         raise RuntimeError("mm_fwd_args layout mismatch between library and binding")
     if lib.mm_decode_args_size() != ctypes.sizeof(DecodeArgs):
@@ -198,6 +195,17 @@ def _dtype_code(t) -> int:
 def _stream_ptr(device) -> int:
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_buf(t, shape, dtype, name, contiguous=False):
+    """A caller-supplied output buffer must have exactly the shape and dtype the kernel
+    writes (it writes the full extent without bounds of its own)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _check_dev(*ts):
@@ -238,21 +246,20 @@ def attn_fwd(q, k, v, scale=None, *, causal=False, score_mod=SCORE_NONE, alibi_s
     """
     torch = _torch()
     lib = load_library()
-    dev = _check_dev(q, k, v, out, lse, alibi_slopes, block_mask, q_doc, kv_doc)
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
     if v.shape != k.shape or Bk != B or Dk != D or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q/k/v shapes or dtypes disagree")
+    fp8 = q.dtype == torch.float8_e4m3fn
+    _check_buf(out, (B, Hq, Sq, D), torch.bfloat16 if fp8 else q.dtype, "out")
+    _check_buf(lse, (B, Hq, Sq), torch.float32, "lse", contiguous=True)
+    dev = _check_dev(q, k, v, out, lse, alibi_slopes, block_mask, q_doc, kv_doc)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    fp8 = q.dtype == torch.float8_e4m3fn
     if out is None:
         out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16 if fp8 else q.dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != (B, Hq, Sq)):
-        raise ValueError("lse must be contiguous fp32 [B,Hq,Sq]")
     a = FwdArgs()
     a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
@@ -306,6 +313,8 @@ def _mods(score_mod, mask_flags, window, rowdrop, alibi_slopes, block_mask, Hq, 
         score_mod = {"none": SCORE_NONE, "alibi": SCORE_ALIBI}[score_mod]
     flags = int(mask_flags)
     if window is not None:
+        if not 0 <= int(window) <= 2 ** 31 - 1:
+            raise ValueError(f"window must lie in [0, 2**31 - 1], got {window}")
         flags |= MASK_WINDOW
     seed, thr = 0, 0
     if rowdrop is not None:
@@ -364,7 +373,6 @@ def attn_bwd(q, k, v, out, lse, dout, scale=None, *, causal=False, score_mod=SCO
     """
     torch = _torch()
     lib = load_library()
-    dev = _check_dev(q, k, v, out, lse, dout, alibi_slopes, block_mask, q_doc, kv_doc, workspace, dq, dk, dv)
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
     if v.shape != k.shape or Bk != B or Dk != D or out.shape != q.shape or dout.shape != q.shape:
@@ -373,6 +381,12 @@ def attn_bwd(q, k, v, out, lse, dout, scale=None, *, causal=False, score_mod=SCO
         raise ValueError("q/k/v/out/dout dtypes disagree")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
         raise ValueError("lse must be contiguous fp32 [B,Hq,Sq]")
+    _check_buf(dq, q.shape, q.dtype, "dq")
+    _check_buf(dk, k.shape, k.dtype, "dk")
+    _check_buf(dv, v.shape, v.dtype, "dv")
+    if workspace is not None and workspace.dtype != torch.float32:
+        raise ValueError("workspace must be a float32 tensor")
+    dev = _check_dev(q, k, v, out, lse, dout, alibi_slopes, block_mask, q_doc, kv_doc, workspace, dq, dk, dv)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dq = torch.empty_like(q) if dq is None else dq
@@ -426,8 +440,12 @@ def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
     """
     torch = _torch()
     lib = load_library()
-    dev = _check_dev(q, k_cache, v_cache, mask, seq_lens, out, lse, workspace, block_table)
     B, Hq, one, D = q.shape
+    _check_buf(out, (B, Hq, 1, D), q.dtype, "out")
+    _check_buf(lse, (B, Hq), torch.float32, "lse", contiguous=True)
+    if workspace is not None and workspace.dtype != torch.float32:
+        raise ValueError("workspace must be a float32 tensor")
+    dev = _check_dev(q, k_cache, v_cache, mask, seq_lens, out, lse, workspace, block_table)
     if block_table is not None:
         _, Hkv, page_size, Dk = k_cache.shape
         if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \

@@ -74,12 +74,12 @@ def _compile(src: str, extra, build_dir: str = BUILD) -> str:
     return obj
 
 
-def build(jobs: int | None = None, resource_usage: bool = False, defines=(), out: str = LIB,
+def build(jobs: int | None = None, resource_usage: bool = False, out: str = LIB,
           build_dir: str = BUILD) -> str:
-    """Compile every source and link ``out``. ``defines``: extra -D macros (tuning variants)."""
+    """Compile every source and link ``out`` (``resource_usage``: print each kernel's
+    register, LDS and spill figures)."""
     os.makedirs(build_dir, exist_ok=True)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
-    extra += [f"-D{d}" for d in defines]
     extra += [f"-DMM_SOURCE_HASH=\"{source_hash()}\""]
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(jobs) as ex:

@@ -15,6 +15,17 @@ namespace {
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
 constexpr int kTargetDecodeBlocks = 1024;  // ~4 workgroups per CU, one resident round
+// Sequence lengths stay below 2^30 so that the kernels' 32-bit index arithmetic (a row
+// plus the window plus one, a key tile's end) cannot overflow.
+constexpr int32_t kMaxSeq = 1 << 30;
+
+// |q_idx - kv_idx| <= max(Sq, Skv) - 1 for every pair, so a window of max(Sq, Skv) keeps
+// every pair exactly as any larger one does; clamping keeps the kernels' window
+// arithmetic in range for windows up to INT32_MAX.
+int32_t clamp_window(int32_t w, int32_t Sq, int32_t Skv) {
+    const int32_t m = Sq > Skv ? Sq : Skv;
+    return w > m ? m : w;
+}
 
 bool bad_strides(const int64_t *s, int n) {
     for (int i = 0; i < n; ++i)
@@ -114,6 +125,7 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
                  a->descale_q > 0.f && a->descale_k > 0.f && a->descale_v > 0.f))
         return MM_ERR_SHAPE;
     if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0) return MM_ERR_SHAPE;
+    if (a->Sq >= kMaxSeq || a->Skv >= kMaxSeq) return MM_ERR_SHAPE;
     if (a->Hq % a->Hkv != 0) return MM_ERR_SHAPE;
     if (a->D != 64 && a->D != 128) return MM_ERR_UNSUPPORTED;
     if (a->mods.score_mod != MM_SCORE_NONE && a->mods.score_mod != MM_SCORE_ALIBI) return MM_ERR_UNSUPPORTED;
@@ -167,7 +179,7 @@ mm_status mm_attn_fwd(const mm_fwd_args *a, void *stream) {
         p.v_descale = a->descale_v;
     }
     p.slopes = a->mods.alibi_slopes;
-    p.window = a->mods.window;
+    p.window = clamp_window(a->mods.window, a->Sq, a->Skv);
     p.rowdrop = (a->mods.mask_flags & MM_MASK_ROWDROP) ? 1 : 0;
     p.rd_seed = a->mods.rowdrop_seed;
     p.rd_thr = a->mods.rowdrop_threshold;
@@ -231,6 +243,7 @@ mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
     if (!a) return MM_ERR_NULL;
     if (a->dtype != MM_F16 && a->dtype != MM_BF16) return MM_ERR_DTYPE;
     if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0) return MM_ERR_SHAPE;
+    if (a->Sq >= kMaxSeq || a->Skv >= kMaxSeq) return MM_ERR_SHAPE;
     if (a->Hq % a->Hkv != 0) return MM_ERR_SHAPE;
     if (a->D != 64 && a->D != 128) return MM_ERR_UNSUPPORTED;
     const bool rows = (int64_t)a->B * a->Hq * a->Sq != 0, keys = (int64_t)a->B * a->Hkv * a->Skv != 0;
@@ -282,7 +295,7 @@ mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
     p.scale = a->scale;
     p.scale_log2 = a->scale * 1.4426950408889634f;
     p.slopes = a->mods.alibi_slopes;
-    p.window = a->mods.window;
+    p.window = clamp_window(a->mods.window, a->Sq, a->Skv);
     p.bm = a->mods.block_mask;
     p.bm_sb = a->mods.block_mask_strides[0];
     p.bm_sh = a->mods.block_mask_strides[1];

@@ -3,9 +3,9 @@
 // One workgroup = NW waves = 32*NW query rows of one (batch, query head); each wave owns
 // 32 rows. The default is 8 waves (256 rows, one workgroup per CU, two waves per SIMD):
 // every K/V tile copied into LDS then serves 256 rows, which halves the L2 -> LDS
-// traffic of a 4-wave layout. Keys/values stream through LDS in tiles of 64 keys in an
-// NST-stage ring (default 2): the tile NST-1 ahead is copied global -> LDS by the DMA
-// path (global_load_lds_dwordx4, no VGPR staging) while the current tile is computed.
+// traffic of a 4-wave layout. Keys/values stream through LDS in tiles of 64 keys in a
+// two-stage ring: the next tile is copied global -> LDS by the DMA path
+// (global_load_lds_dwordx4, no VGPR staging) while the current tile is computed.
 //
 // Both products run on the 32x32x16 MFMA with fp32 accumulation, in transposed form
 // so that a lane always owns one query row:
@@ -65,11 +65,7 @@ struct Tile {
     __host__ __device__ static constexpr int off(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
 };
 
-#ifndef MM_FWD_NW
-#define MM_FWD_NW 8  // waves per workgroup without a mask mod
-#endif
-
-template <typename TT, int D, bool ALIBI, int MASK, int NW, int NST>
+template <typename TT, int D, bool ALIBI, int MASK, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
     constexpr int BM = 32 * NW, BN = 64;
@@ -84,17 +80,15 @@ void fwd_mfma_kernel(FwdParams p) {
     constexpr float kRescaleSum = 256.f;            // 2^kRescale: bound on a plain tile's lane sum
     typedef typename TT::vec8 V8;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
-    static_assert(NST == 2 || NST == 3, "stages");
 
-    // NST K/V buffers as distinct LDS objects: the loop below is unrolled by NST so every
-    // tile reads a statically known buffer while the DMA fills another, and the compiler
-    // can see the reads never alias the in-flight copies (no early vmcnt wait).
+    // The two K/V buffers as distinct LDS objects: the loop below is unrolled by two so
+    // every tile reads a statically known buffer while the DMA fills the other, and the
+    // compiler can see the reads never alias the in-flight copies (no early vmcnt wait).
     // (one object per stage, K then V: the waitcnt pass tracks only a few DMA targets)
     __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
     __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kv2[NST > 2 ? 2 * TILEB : 16];
-    unsigned char *const KB[3] = {kv0, kv1, kv2};
-    unsigned char *const VB[3] = {kv0 + TILEB, kv1 + TILEB, kv2 + (NST > 2 ? TILEB : 0)};
+    unsigned char *const KB[2] = {kv0, kv1};
+    unsigned char *const VB[2] = {kv0 + TILEB, kv1 + TILEB};
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -492,31 +486,18 @@ void fwd_mfma_kernel(FwdParams p) {
             if (cur < nkb) nxt = next_block(cur + 1, nv);
         }
     } else {
-        if (kt_lo < kt_hi) {
-#pragma unroll
-            for (int st = 0; st < NST - 1; ++st) load_tile(min(kt_lo + st, kt_hi - 1), KB[st], VB[st]);
-        }
+        if (kt_lo < kt_hi) load_tile(kt_lo, KB[0], VB[0]);
         kv_barrier<0>();
-        for (int kt = kt_lo; kt < kt_hi; kt += NST) {
+        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
 #pragma unroll
-            for (int st = 0; st < NST; ++st) {
-                if (NST == 2) {
-                    if (kt + st < kt_hi) {
-                        tile(kt + st, 1, KB[st], VB[st], kt + st + 1 < kt_hi ? kt + st + 1 : -1,
-                             KB[(st + 1) % NST], VB[(st + 1) % NST]);
-                        kv_barrier<0>();
-                    }
-                } else {
-                    // three stages: always copy (past the end: the last tile again, into a
-                    // buffer nobody reads) so the waits are uniform; the copies issued
-                    // during this tile stay in flight, the next tile's must have landed
-                    tile(kt + st, 1, KB[st], VB[st], min(kt + st + NST - 1, kt_hi - 1),
-                         KB[(st + NST - 1) % NST], VB[(st + NST - 1) % NST]);
-                    kv_barrier<2 * LOADS>();
+            for (int st = 0; st < 2; ++st) {
+                if (kt + st < kt_hi) {
+                    tile(kt + st, 1, KB[st], VB[st], kt + st + 1 < kt_hi ? kt + st + 1 : -1,
+                         KB[st ^ 1], VB[st ^ 1]);
+                    kv_barrier<0>();
                 }
             }
         }
-        if (NST > 2) kv_barrier<0>();  // drain the copies issued past the end
     }
 
     // ---- epilogue ----
@@ -546,27 +527,17 @@ void fwd_mfma_kernel(FwdParams p) {
 }
 
 
-#ifndef MM_FWD_NW_MASKED
-#define MM_FWD_NW_MASKED 4  // window, document or block masks: finer row tiles skip more keys
-#endif
-#ifndef MM_FWD_NW_CAUSAL
-#define MM_FWD_NW_CAUSAL 8  // causal alone on long rows: the shared tiles outweigh the idle diagonal waves
-#endif
-#ifndef MM_FWD_NST
-#define MM_FWD_NST 2
-#endif
-
-#ifndef MM_FWD_CAUSAL_SHORT
-#define MM_FWD_CAUSAL_SHORT 4096  // causal, D = 128: at most this many visible keys -> 4 waves
-#endif
+constexpr int kFwdNW = 8;          // waves per workgroup without a mask mod
+constexpr int kFwdNWMasked = 4;    // window, document or block masks: finer row tiles skip more keys
+constexpr int kFwdNWCausal = 8;    // causal alone on long rows: the shared tiles outweigh the idle diagonal waves
+constexpr int kFwdCausalShort = 4096;  // causal, D = 128: at most this many visible keys -> 4 waves
 
 template <typename TT, int D, bool A, int M, int NW>
 hipError_t launch_fwd_mfma_nw(FwdParams p, hipStream_t s) {
-    constexpr int NST = MM_FWD_NST;
     static_assert(!(M & MASK_BLOCK) || NW == 4, "block masks use 128-row workgroups");
     p.n_qtiles = (p.Sq + 32 * NW - 1) / (32 * NW);
     const dim3 grid((unsigned)(p.n_qtiles * p.Hq * p.B)), block(64 * NW);
-    fwd_mfma_kernel<TT, D, A, M, NW, NST><<<grid, block, 0, s>>>(p);
+    fwd_mfma_kernel<TT, D, A, M, NW><<<grid, block, 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -581,9 +552,8 @@ hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
     // are 128 rows, one 4-wave workgroup each. D = 64 always takes 4: its halved tile
     // products leave the shared copies less to gain (no mod 7-15% faster at S 2048 to
     // 8192, causal 6-15%, alibi 0-3%)
-    constexpr int NW = D == 64 ? 4
-                               : (M == 0 ? MM_FWD_NW : (M == MASK_CAUSAL ? MM_FWD_NW_CAUSAL : MM_FWD_NW_MASKED));
-    if (M == MASK_CAUSAL && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= MM_FWD_CAUSAL_SHORT)
+    constexpr int NW = D == 64 ? 4 : (M == 0 ? kFwdNW : (M == MASK_CAUSAL ? kFwdNWCausal : kFwdNWMasked));
+    if (M == MASK_CAUSAL && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= kFwdCausalShort)
         return launch_fwd_mfma_nw<TT, D, A, M, 4>(p, s);
     return launch_fwd_mfma_nw<TT, D, A, M, NW>(p, s);
 }

@@ -190,11 +190,13 @@ def random_f16_bias(seed: int, shape) -> np.ndarray:
     return f32_to_bits(rng(seed).standard_normal(size=shape, dtype=np.float32), "f16")
 
 
-def sample_rows(seed: int, B: int, H: int, S: int, n_random: int = 64) -> np.ndarray:
+def sample_rows(seed: int, B: int, H: int, S: int, n_random: int = 64, block: int = 128) -> np.ndarray:
     """Flat row ids r = (b*H + h)*S + i for sampled parity at full size.
 
-    Every (b, h) contributes its first and last row; n_random more rows are drawn
-    uniformly over all rows. Sorted and unique.
+    Every (b, h) contributes its first and last row and one row drawn uniformly inside
+    each block of ``block`` consecutive rows (0 = none): with the smallest query tile of
+    the forward launches, every workgroup of a launch has a checked row. n_random more
+    rows are drawn uniformly over all rows. Sorted and unique.
     """
     g = rng(seed)
     rows = []
@@ -202,6 +204,11 @@ def sample_rows(seed: int, B: int, H: int, S: int, n_random: int = 64) -> np.nda
         rows.append(bh * S)
         rows.append(bh * S + S - 1)
     rows.extend(g.integers(0, B * H * S, size=n_random).tolist())
+    if block > 0 and S > 0:
+        starts = np.arange(0, S, block, dtype=np.int64)
+        span = np.minimum(starts + block, S) - starts
+        for bh in range(B * H):
+            rows.extend((bh * S + starts + (g.random(starts.size) * span).astype(np.int64)).tolist())
     return np.unique(np.asarray(rows, dtype=np.int64))
 
 

@@ -43,8 +43,7 @@ def test_library_built_from_these_sources():
     a mismatch at load, so a stale build cannot run)."""
     from mask_mods_amd.build import source_hash
     lib = mm.load_library()
-    if mm.library_path() == mm._DEFAULT_LIB:
-        assert lib.mm_source_hash().decode() == source_hash()
+    assert lib.mm_source_hash().decode() == source_hash()
     assert len(source_hash()) == 16
 
 
@@ -84,6 +83,8 @@ def _fwd(**kw):
     (dict(Hkv=0), SHAPE),
     (dict(Sq=-1), SHAPE),
     (dict(Skv=-5), SHAPE),
+    (dict(Sq=1 << 30), SHAPE),                   # lengths stay below 2^30
+    (dict(Skv=1 << 30), SHAPE),
     (dict(D=96), UNSUP),
     (dict(D=256), UNSUP),
     (dict(mods_score_mod=9), UNSUP),
@@ -267,6 +268,8 @@ def _bwd(**kw):
     (dict(dtype=0), DTYPE),                      # the backward is 16-bit only
     (dict(dtype=3), DTYPE),
     (dict(Hq=3), SHAPE),
+    (dict(Sq=1 << 30), SHAPE),
+    (dict(Skv=1 << 30), SHAPE),
     (dict(D=32), UNSUP),
     (dict(mods_mask_flags=16), UNSUP),
     (dict(do_strides=mm._I64x3(0, 0, 12)), STRIDE),

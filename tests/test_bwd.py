@@ -80,6 +80,20 @@ def test_matrix(dtype, D, case):
     _check(1, 2, 2, 250, 250, D, dtype, seed=1, **CASES[case])
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_int32_max_window_with_causal(D):
+    """A window of 2**31 - 1 together with causal keeps exactly the causal pairs (its
+    bound arithmetic must not wrap into an empty key range): the gradients match the
+    oracle's, and the plain causal backward's."""
+    import torch
+    W = 2 ** 31 - 1
+    g1 = _check(1, 2, 2, 300, 300, D, "bf16", seed=41, causal=True, window=W)
+    (g2, _, _) = _grads(1, 2, 2, 300, 300, D, "bf16", seed=41, causal=True)
+    for a, b_ in zip(g1, g2):
+        assert torch.allclose(a.float(), b_.float(), atol=2e-2, rtol=2e-2)
+        assert a.abs().max() > 0
+
+
 def test_multi_tile_1024():
     _check(1, 2, 2, 1024, 1024, 128, "bf16", seed=2, causal=True, alibi=True)
 

@@ -188,6 +188,22 @@ def test_scores_rising_along_keys(dtype, D, causal):
     _run(1, 2, 2, S, S, D, dtype, causal=causal, x=x)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_int32_max_window_equals_no_mask(D):
+    """A window of 2**31 - 1 keeps every pair (its bound arithmetic must not wrap): the
+    result matches the oracle without a mask, and the unmasked kernel."""
+    import torch
+    import mask_mods_amd as mm
+    W = 2 ** 31 - 1
+    x = inputs.attention_inputs(12, 1, 2, 2, 333, 333, D, "bf16")
+    _run(1, 2, 2, 333, 333, D, "bf16", window=W, x=x)
+    q, k, v = (to_torch(x[n], "bf16") for n in ("q", "k", "v"))
+    o1, l1 = mm.attn_fwd(q, k, v, 0.1)
+    o2, l2 = mm.attn_fwd(q, k, v, 0.1, window=W)
+    torch.cuda.synchronize()
+    assert torch.allclose(o1.float(), o2.float(), atol=1e-2) and torch.allclose(l1, l2, atol=1e-4)
+
+
 def test_large_window_equals_no_mask():
     import torch
     import mask_mods_amd as mm
@@ -210,9 +226,11 @@ def test_config_dense_bf16_sampled(S, causal):
     _run(2, 32, 32, S, S, 128, "bf16", causal=causal, seed=2, rows=_sample(2, 32, S, 2))
 
 
+@pytest.mark.parametrize("S", [2048, 4096, 8192])
 @pytest.mark.parametrize("case", ["alibi", "sliding_window", "causal_via_mask"])
-def test_config_mods_bf16_8192_sampled(case):
-    S = 8192
+def test_config_mods_bf16_sampled(case, S):
+    """The flex mods at the dense workload's shapes: B2 H32 D128, S 2048 / 4096 / 8192
+    (at 4096 and below the causal mask runs 4-wave workgroups, at 8192 8-wave ones)."""
     _run(2, 32, 32, S, S, 128, "bf16", seed=3, rows=_sample(2, 32, S, 3), **CASES[case])
 
 
