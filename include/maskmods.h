@@ -246,6 +246,31 @@ size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t
  * a missing or short workspace. */
 mm_status mm_attn_decode(const mm_decode_args *args, void *stream);
 
+/* Bytes of the decode scratch that the library holds on each GPU for
+ * mm_attn_decode_noalloc (16 MiB). */
+#define MM_DECODE_SCRATCH_BYTES (16u * 1024u * 1024u)
+
+/* Decode attention that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The operation, kernels, split count and results are
+ * those of mm_attn_decode with the same arguments; args->workspace and
+ * args->workspace_bytes are ignored. The split partials (the B * Hq * splits * (D + 2)
+ * floats that mm_attn_decode_workspace_size counts) go to a static device array of
+ * MM_DECODE_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends; its address is looked up once per device, on the first call with that
+ * device current. No device memory is allocated or freed by any call.
+ *   - A call whose partials need more than MM_DECODE_SCRATCH_BYTES returns
+ *     MM_ERR_WORKSPACE and launches nothing (with the automatic split count that
+ *     happens only beyond B * Hq = 32263 at D 128, 63550 at D 64).
+ *   - `stream` must belong to the calling thread's current device; otherwise, or if the
+ *     address lookup fails, the call returns MM_ERR_LAUNCH and launches nothing.
+ *   - Every call on a GPU uses that GPU's one array, which keeps the last call's
+ *     partials (each call writes every partial it reads, so nothing needs clearing).
+ *     Calls that overlap in time on one GPU (on different streams, or from threads
+ *     without ordering) race and give undefined results: order them, e.g. on one stream.
+ * Other rejections as mm_attn_decode. Two launches on `stream`. */
+mm_status mm_attn_decode_noalloc(const mm_decode_args *args, void *stream);
+
 /* Split count mm_attn_decode uses when num_splits == 0: about one resident round of
  * split workgroups (1024 with one query head per workgroup, 512 with 2 or 4), at least
  * 256 keys per split, at most 256 splits, a multiple of 8 (when 8 or more) if a kv

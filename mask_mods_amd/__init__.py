@@ -17,7 +17,8 @@ import math
 import os
 
 __all__ = [
-    "attn_fwd", "attn_bwd", "bwd_workspace_size", "attn_decode", "decode_workspace_size",
+    "attn_fwd", "attn_bwd", "bwd_workspace_size", "attn_decode", "attn_decode_noalloc",
+    "decode_workspace_size", "DECODE_SCRATCH_BYTES",
     "decode_auto_splits", "block_mask_create",
     "MaskModsError", "library_path", "load_library",
     "SCORE_NONE", "SCORE_ALIBI", "MASK_CAUSAL", "MASK_WINDOW", "MASK_ROWDROP",
@@ -34,6 +35,8 @@ ROWDROP_5PCT = int(0.05 * 2 ** 32)  # threshold that drops ~5% of rows
 # block mask: query rows x keys per block, and the per-block classes
 BLOCK_Q, BLOCK_KV = 128, 64
 BLOCK_EMPTY, BLOCK_PARTIAL, BLOCK_FULL = 0, 1, 2
+# bytes of the static per-GPU decode scratch of mm_attn_decode_noalloc
+DECODE_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _STATUS = {
     0: "MM_OK", -1: "MM_ERR_NULL", -2: "MM_ERR_SHAPE", -3: "MM_ERR_DTYPE",
@@ -142,6 +145,8 @@ def load_library():
     lib.mm_attn_fwd.restype = ctypes.c_int32
     lib.mm_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
     lib.mm_attn_decode.restype = ctypes.c_int32
+    lib.mm_attn_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+    lib.mm_attn_decode_noalloc.restype = ctypes.c_int32
     lib.mm_attn_decode_workspace_size.argtypes = [ctypes.c_int32] * 6
     lib.mm_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.mm_attn_decode_auto_splits.argtypes = [ctypes.c_int32] * 4
@@ -425,9 +430,20 @@ def decode_auto_splits(B, Hq, kv_len, Hkv=None) -> int:
     return int(load_library().mm_attn_decode_auto_splits(B, Hq, Hkv, kv_len))
 
 
+def attn_decode_noalloc(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
+                        return_lse=True, num_splits=0, out=None, lse=None, block_table=None):
+    """attn_decode through mm_attn_decode_noalloc: the split partials go to the library's
+    static per-GPU scratch (DECODE_SCRATCH_BYTES) instead of a workspace, so the call
+    allocates no device memory when ``out`` (and ``lse``, or return_lse=False) are
+    given. Calls that overlap in time on one GPU share the scratch and race."""
+    return attn_decode(q, k_cache, v_cache, kv_len, scale, mask=mask, seq_lens=seq_lens,
+                       return_lse=return_lse, num_splits=num_splits, out=out, lse=lse,
+                       block_table=block_table, _noalloc=True)
+
+
 def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
                 return_lse=True, num_splits=0, workspace=None, out=None, lse=None,
-                block_table=None):
+                block_table=None, _noalloc=False):
     """Decode attention: q [B,Hq,1,D] against caches [B,Hkv,Scap,D] (f16/bf16).
 
     kv_len: number of cache positions in use (<= Scap). mask: optional f16
@@ -471,8 +487,8 @@ def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
         out = torch.empty((B, Hq, 1, D), dtype=q.dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    need = lib.mm_attn_decode_workspace_size(B, Hq, Hkv, int(kv_len), D, int(num_splits))
-    if workspace is None:
+    if not _noalloc and workspace is None:
+        need = lib.mm_attn_decode_workspace_size(B, Hq, Hkv, int(kv_len), D, int(num_splits))
         workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=dev)
     a = DecodeArgs()
     a.q, a.k_cache, a.v_cache, a.out = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr()
@@ -486,14 +502,16 @@ def attn_decode(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,
     a.kv_strides = _I64x3(*k_cache.stride()[:3])
     a.o_strides = _I64x2(*out.stride()[:2])
     a.mask_strides = _I64x2(*(mask.stride()[:2] if mask is not None else (0, 0)))
-    a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.num_splits = int(num_splits)
     if block_table is not None:
         a.block_table = block_table.data_ptr()
         a.block_table_stride = block_table.stride(0)
         a.page_size = int(page_size)
-    st = lib.mm_attn_decode(ctypes.byref(a), _stream_ptr(dev))
+    fn, name = (lib.mm_attn_decode_noalloc, "mm_attn_decode_noalloc") if _noalloc else (lib.mm_attn_decode, "mm_attn_decode")
+    st = fn(ctypes.byref(a), _stream_ptr(dev))
     if st != 0:
-        raise MaskModsError(st, "mm_attn_decode")
+        raise MaskModsError(st, name)
     return out, (lse if return_lse else None)

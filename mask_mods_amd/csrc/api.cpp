@@ -6,11 +6,46 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kernels.h"
 
 using namespace mm;
 
+// The split partials of mm_attn_decode_noalloc: one static array per GPU, resident until
+// the process ends. Host code never uses this name as an address (on the host it is
+// only a stand-in); scratch_address() looks the device address up once per device.
+static __device__ __align__(256) unsigned char scratch[MM_DECODE_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up (with that device
+// current) on the first call per device and kept; nullptr if the lookup fails or
+// `stream` belongs to another device.
+void *scratch_address(hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return nullptr;
+    }
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+        void *found = nullptr;
+        if (hipGetSymbolAddress(&found, HIP_SYMBOL(scratch)) != hipSuccess || !found) return nullptr;
+        g_scratch_ptr[dev].store(found, std::memory_order_release);
+        ptr = found;
+    }
+    return ptr;
+}
 
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
@@ -330,7 +365,13 @@ size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t
     return (size_t)B * Hq * splits * (size_t)(D + 2) * sizeof(float);
 }
 
-mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// mm_attn_decode and mm_attn_decode_noalloc: the same checks and launches; the second
+// puts the partials in the static scratch instead of the caller's workspace.
+mm_status decode_impl(const mm_decode_args *a, void *stream, bool static_scratch) {
     if (!a) return MM_ERR_NULL;
     if (a->B != 0 && (!a->q || !a->out)) return MM_ERR_NULL;
     if (a->B != 0 && a->kv_len > 0 && (!a->k_cache || !a->v_cache)) return MM_ERR_NULL;
@@ -359,8 +400,16 @@ mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
 
     const int splits = decode_splits(a->B, a->Hq, a->Hkv, a->kv_len, a->num_splits);
     const size_t need = (size_t)a->B * a->Hq * splits * (size_t)(a->D + 2) * sizeof(float);
-    if (!a->workspace || a->workspace_bytes < need) return MM_ERR_WORKSPACE;
-    if (misaligned16(a->workspace)) return MM_ERR_WORKSPACE;
+    void *workspace = a->workspace;
+    size_t workspace_bytes = a->workspace_bytes;
+    if (static_scratch) {
+        if (need > (size_t)MM_DECODE_SCRATCH_BYTES) return MM_ERR_WORKSPACE;
+        workspace = scratch_address((hipStream_t)stream);
+        if (!workspace) return MM_ERR_LAUNCH;
+        workspace_bytes = MM_DECODE_SCRATCH_BYTES;
+    }
+    if (!workspace || workspace_bytes < need) return MM_ERR_WORKSPACE;
+    if (misaligned16(workspace)) return MM_ERR_WORKSPACE;
 
     DecParams p = {};
     p.q = a->q;
@@ -388,7 +437,7 @@ mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
     p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1];
     p.m_sb = a->mask_strides[0]; p.m_sh = a->mask_strides[1];
     p.scale_log2 = a->scale * 1.4426950408889634f;
-    float *ws = (float *)a->workspace;
+    float *ws = (float *)workspace;
     const size_t nrow = (size_t)a->B * a->Hq * splits;
     p.ws_o = ws;
     p.ws_m = ws + nrow * a->D;
@@ -401,5 +450,13 @@ mm_status mm_attn_decode(const mm_decode_args *a, void *stream) {
     const hipError_t e = launch_decode(p, a->dtype, a->D, (hipStream_t)stream);
     return e == hipSuccess ? MM_OK : MM_ERR_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_attn_decode(const mm_decode_args *a, void *stream) { return decode_impl(a, stream, false); }
+
+mm_status mm_attn_decode_noalloc(const mm_decode_args *a, void *stream) { return decode_impl(a, stream, true); }
 
 }  // extern "C"

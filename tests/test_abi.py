@@ -290,3 +290,24 @@ def test_bwd_workspace_size():
     # lse2 and D per row, rows padded to 64 per (b, h)
     assert mm.bwd_workspace_size(2, 3, 100) == 2 * 2 * 3 * 128 * 4
     assert mm.bwd_workspace_size(1, 1, 0) == 0
+
+
+def test_decode_noalloc_rejects_oversize_before_any_device_work():
+    """mm_attn_decode_noalloc refuses, before touching a device, a call whose partials
+    exceed the static scratch; calls with nothing to do return OK."""
+    lib = mm.load_library()
+    a = mm.DecodeArgs()
+    a.q = a.k_cache = a.v_cache = a.out = FAKE
+    a.dtype = 1
+    a.B, a.Hq, a.Hkv, a.kv_len, a.Scap, a.D = 4, 32, 32, 8192, 8192, 128
+    a.scale = 0.088
+    a.q_strides = mm._I64x2(32 * 128, 128)
+    a.kv_strides = mm._I64x3(32 * 8192 * 128, 8192 * 128, 128)
+    a.o_strides = mm._I64x2(32 * 128, 128)
+    a.num_splits = 256  # 4*32*256*130*4 bytes > 16 MiB
+    assert 4 * 32 * 256 * 130 * 4 > mm.DECODE_SCRATCH_BYTES
+    assert lib.mm_attn_decode_noalloc(ctypes.byref(a), None) == WORKSPACE
+    a.B = 0
+    assert lib.mm_attn_decode_noalloc(ctypes.byref(a), None) == OK
+    a.B, a.D = 4, 96
+    assert lib.mm_attn_decode_noalloc(ctypes.byref(a), None) == UNSUP
