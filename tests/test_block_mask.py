@@ -210,16 +210,28 @@ def test_config_8192_half_sparse_sampled(pred):
     _run(B, H, H, S, S, 128, "bf16", bm, seed=14, rows=rows, **PREDS[pred])
 
 
-def test_config_8192_causal_block_mask_bitwise():
-    """The created causal classes at full size give the plain causal kernel's bits."""
+def test_config_8192_causal_block_mask_matches_plain():
+    """The created causal classes at full size against the plain causal kernel. Past 4096
+    keys the plain causal forward at D 128 runs the software-pipelined kernel, whose sums
+    run in another order, so the two agree to the parity bar rather than to the bit (at
+    2000 keys, test_created_mask_equals_predicates_alone holds them to the bit); both
+    match the oracle on sampled rows."""
     import torch
     import mask_mods_amd as mm
     B, H, S = 2, 32, 8192
-    print(f"[block] causal bitwise B={B} H={H} S={S}", flush=True)
+    print(f"[block] causal vs plain B={B} H={H} S={S}", flush=True)
     x = inputs.attention_inputs(15, B, H, H, S, S, 128, "bf16")
     q, k, v = (to_torch(x[n], "bf16") for n in ("q", "k", "v"))
     bm = mm.block_mask_create(S, S, causal=True)
-    o1, l1 = mm.attn_fwd(q, k, v, causal=True, block_mask=bm)
-    o2, l2 = mm.attn_fwd(q, k, v, causal=True)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    o1, l1 = mm.attn_fwd(q, k, v, scale, causal=True, block_mask=bm)
+    o2, l2 = mm.attn_fwd(q, k, v, scale, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert_parity(to_f64(o1), to_f64(o2), O_ATOL, O_RTOL, "O block vs plain")
+    assert_parity(to_f64(l1), to_f64(l2), LSE_ATOL, LSE_RTOL, "LSE block vs plain")
+    rows = inputs.sample_rows(15, B, H, S, n_random=16)
+    O, L = oracle.attention(*(inputs.bits_to_f64(x[n], "bf16") for n in ("q", "k", "v")), scale=scale,
+                            causal=True, rows=rows)
+    for o, l in ((o1, l1), (o2, l2)):
+        assert_parity(to_f64(o).reshape(-1, 128)[rows], O, O_ATOL, O_RTOL, "O")
+        assert_parity(to_f64(l).reshape(-1)[rows], L, LSE_ATOL, LSE_RTOL, "LSE")

@@ -204,6 +204,18 @@ def test_int32_max_window_equals_no_mask(D):
     assert torch.allclose(o1.float(), o2.float(), atol=1e-2) and torch.allclose(l1, l2, atol=1e-4)
 
 
+@pytest.mark.parametrize("dtype,S,causal,rise", [("bf16", 1100, False, 6.0), ("f16", 1100, False, 3.0),
+                                                  ("bf16", 4500, True, 3.0), ("f16", 4500, True, 1.0)])
+def test_scores_far_above_the_first_block(dtype, S, causal, rise):
+    """D 128 without a mask, or causal past 4096 keys (the software-pipelined kernel): the
+    scores climb far above the first key block's max (past 2^64 in probability for bf16,
+    2^15 for f16), so the first pass fails its bound and the workgroup takes the max
+    sweep and the recompute."""
+    print(f"[fwd far-rising] {dtype} S={S} causal={causal} rise={rise}", flush=True)
+    x = inputs.rising_score_inputs(32, 1, 2, S, 128, dtype, rise=rise)
+    _run(1, 2, 2, S, S, 128, dtype, causal=causal, x=x)
+
+
 def test_large_window_equals_no_mask():
     import torch
     import mask_mods_amd as mm
