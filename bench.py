@@ -7,9 +7,13 @@ One step = one pass of the whole path over one batch of synthetic input:
 Inputs are seeded N(0,1) (mask_mods_amd.inputs) and resident in HBM before timing.
 
 Printed: one JSON line with the forward TFLOP/s as `value`, its roofline (MFMA
-bound) and the decode GB/s with its roofline (HBM bound), the other flex cases at
-S=8192 for context, and the CPU oracle timed on a bounded sample of the same
-forward workload on this host's cores.
+bound) and the decode GB/s with its roofline (HBM bound); the two headline calls
+again by the pages' report method (10 warmup calls, 12 samples of 100 calls, mean,
+std, CV); the other flex cases at S=8192, 4096 and 2048 and at D=64; GQA
+cross-attention; decode at KV lengths 1, 17, 1000 and 4096, GQA, paged and a
+mixed-length batch of 8; the backward; and the CPU oracle timed on a bounded sample
+of the forward workload, on the tiny fp32 workload and on the full decode call, on
+this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -35,12 +39,16 @@ PAGES_NO_MOD_MI300X_TFLOPS = 470.1  # FlyDSL PR #931 report, no_mod at this work
 
 FWD = dict(B=2, H=32, S=8192, D=128)
 DEC = dict(B=1, H=32, L=32768, D=128)
-FWD_KERNEL = "fwd_mfma_kernel"
+FWD_KERNEL = "fwd_pipe_kernel"  # the headline (D 128, no mod) runs the software-pipelined forward
 DEC_KERNELS = ("decode_split_kernel", "decode_merge_kernel")
 FP8_KERNEL = "fwd_fp8_kernel"
-KERNEL_SOURCES = ["mask_mods_amd/csrc/fwd_mfma.h", "mask_mods_amd/csrc/fwd_fp8.h",
+KERNEL_SOURCES = ["mask_mods_amd/csrc/fwd_pipe.h", "mask_mods_amd/csrc/fwd_tile.h",
+                  "mask_mods_amd/csrc/fwd_mfma.h", "mask_mods_amd/csrc/fwd_fp8.h",
                   "mask_mods_amd/csrc/fwd_common.h", "mask_mods_amd/csrc/common.h",
                   "mask_mods_amd/csrc/decode.hip", "mask_mods_amd/csrc/kernels.h"]
+# the pages' report method (FlyDSL PR, Performance Report): warmup 10, then 12 samples of
+# 100 iterations each, mean +- std and the coefficient of variation
+PAGES_WARMUP, PAGES_SAMPLES, PAGES_ITERS = 10, 12, 100
 
 
 def kernel_source_hash() -> str:
@@ -87,7 +95,29 @@ def load_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(x, target_s=10.0):
+def cpu_configs(xd):
+    """The oracle on the tiny fp32 workload and on the headline decode call, each in full."""
+    import oracle
+    from mask_mods_amd import inputs
+    out = {}
+    x = inputs.attention_inputs(0, 1, 2, 2, 128, 128, 64, "f32")
+    args = [inputs.bits_to_f64(x[n], "f32") for n in ("q", "k", "v")]
+    t0 = time.perf_counter()
+    for _ in range(10):
+        oracle.attention(*args, scale=0.125)
+    dt = (time.perf_counter() - t0) / 10
+    out["tiny_fp32_b1_h2_s128_d64"] = {"seconds": dt, "note": "full workload, mean of 10 calls"}
+    Bd, Hd, L, Dd = DEC["B"], DEC["H"], DEC["L"], DEC["D"]
+    qd, kd, vd = (inputs.bits_to_f64(xd[n], "f16") for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    oracle.attention(qd, kd, vd, scale=0.08837890625, Skv=L, add_mask=inputs.bits_to_f64(xd["mask"], "f16"))
+    dt = time.perf_counter() - t0
+    out["decode_f16_b1_h32_d128_l32768"] = {"seconds": dt, "GBs": dec_bytes(Bd, Hd, L, Dd) / dt / 1e9,
+                                            "note": "full workload, one call"}
+    return out
+
+
+def cpu_baseline(x, target_s=10.0, xd=None):
     """Time the oracle on random rows of the forward workload (bounded sample)."""
     import oracle
     from mask_mods_amd import inputs
@@ -106,11 +136,14 @@ def cpu_baseline(x, target_s=10.0):
     oracle.attention(qd, kd, vd, scale=scale, rows=rows)
     dt = time.perf_counter() - t0
     flops = n * 4.0 * S * D
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} random query rows of the B2 H32 D128 S8192 bf16 no-mod forward "
-                      f"(each row against all {S} keys), fp64, {dt:.1f} s; full workload "
-                      f"extrapolates to {B * H * S / (n / dt):.0f} s",
-            "seconds": dt}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} random query rows of the B2 H32 D128 S8192 bf16 no-mod forward "
+                     f"(each row against all {S} keys), fp64, {dt:.1f} s; full workload "
+                     f"extrapolates to {B * H * S / (n / dt):.0f} s",
+           "seconds": dt}
+    if xd is not None:
+        res["full_configs"] = cpu_configs(xd)
+    return res
 
 
 COPY_BYTES = 1 << 30  # --only copy: 1 GiB read and 1 GiB written per call
@@ -179,6 +212,38 @@ def to_fp8(t, torch):
     """Per-tensor e4m3 quantisation on the device: (t / s) rounded, s = max|t| / 448."""
     s = (t.float().abs().max() / 448.0).item()
     return (t.float() / s).to(torch.float8_e4m3fn), s
+
+
+def time_calls(torch, stream, fn, n=20, warmup=5):
+    """Mean seconds per call of fn over n calls after warmup (HIP events on the stream)."""
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3
+
+
+def pages_stats(torch, stream, fn):
+    """The pages' method: PAGES_WARMUP calls, then PAGES_SAMPLES samples of PAGES_ITERS
+    calls each; per-call time in microseconds, mean +- std over samples, CV in percent."""
+    for _ in range(PAGES_WARMUP):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(PAGES_SAMPLES)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        for _ in range(PAGES_ITERS):
+            fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([e0.elapsed_time(e1) / PAGES_ITERS * 1e3 for e0, e1 in ev])
+    return {"mean_us": round(float(us.mean()), 2), "std_us": round(float(us.std()), 2),
+            "cv_pct": round(float(us.std() / us.mean() * 100), 2),
+            "method": f"{PAGES_WARMUP} warmup, {PAGES_SAMPLES} samples x {PAGES_ITERS} calls"}
 
 
 def profile_one(args, torch, mm, inputs, dev):
@@ -337,6 +402,11 @@ def main():
     dec_avg_s = dec_ms.mean() * 1e-3
     gbs = dbytes / dec_avg_s / 1e9
 
+    # the pages' report method on the two headline calls: mean +- std over 12 samples of
+    # 100 calls after 10 warmup calls, and the coefficient of variation
+    fwd_pages = pages_stats(torch, stream, fwd)
+    dec_pages = pages_stats(torch, stream, dec)
+
     # ---- other flex cases at the same shape (context; same kernel family)
     cases = {}
     if not args.no_cases:
@@ -400,28 +470,39 @@ def main():
             ent["latency_vs_no_mod"] = round(t / fwd_avg_s, 3)
             cases[name] = ent
 
-    # ---- the dense workload's shorter lengths: S 2048 and 4096, no mod and causal
+    # ---- the dense workload's shorter lengths with every flex case (S 2048 and 4096), and
+    # the D 64 variant (S 2048 and 8192): the pages' tables report each case at each length
     scases = {}
     if not args.no_cases:
-        for Ss in (2048, 4096):
-            xs = inputs.attention_inputs(2, B, H, H, Ss, Ss, D, "bf16")
-            sq_, sk_, sv_ = (dev_tensor(xs[n], "bf16") for n in ("q", "k", "v"))
-            sout = torch.empty_like(sq_)
-            slse = torch.empty(B, H, Ss, dtype=torch.float32, device=dev)
-            for cname, causal in (("no_mod", False), ("causal", True)):
-                for _ in range(5):
-                    mm.attn_fwd(sq_, sk_, sv_, scale, causal=causal, out=sout, lse=slse)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                n = 20
-                e0.record(stream)
-                for _ in range(n):
-                    mm.attn_fwd(sq_, sk_, sv_, scale, causal=causal, out=sout, lse=slse)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                t = e0.elapsed_time(e1) / n * 1e-3
-                alg = fwd_flops(B, H, Ss, Ss, D, causal=causal)
-                scases[f"s{Ss}_{cname}"] = {"us": round(t * 1e6, 1), "tflops_algorithmic": round(alg / t / 1e12, 1),
-                                            "frac_bf16_peak": round(alg / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        W = 256
+        short = {"no_mod": dict(), "causal": dict(causal=True), "alibi": dict(score_mod=mm.SCORE_ALIBI),
+                 "sliding_window": dict(window=W, mask_flags=mm.MASK_CAUSAL),
+                 "causal_via_mask": dict(mask_flags=mm.MASK_CAUSAL)}
+        for Ds, lens, names in ((D, (2048, 4096), list(short)), (64, (2048, 8192), ["no_mod", "causal", "alibi"])):
+            for Ss in lens:
+                xs = inputs.attention_inputs(2, B, H, H, Ss, Ss, Ds, "bf16")
+                sq_, sk_, sv_ = (dev_tensor(xs[n], "bf16") for n in ("q", "k", "v"))
+                sout = torch.empty_like(sq_)
+                slse = torch.empty(B, H, Ss, dtype=torch.float32, device=dev)
+                ss_ = float(np.float32(1.0 / math.sqrt(Ds)))
+                t_nomod = None
+                for cname in names:
+                    kw = short[cname]
+                    t = time_calls(torch, stream, lambda: mm.attn_fwd(sq_, sk_, sv_, ss_, out=sout, lse=slse, **kw))
+                    dense = fwd_flops(B, H, Ss, Ss, Ds)
+                    if cname in ("causal", "causal_via_mask"):
+                        alg = dense / 2
+                    elif cname == "sliding_window":
+                        alg = 4.0 * B * H * Ds * window_pairs(Ss, W)
+                    else:
+                        alg = dense
+                    t_nomod = t if cname == "no_mod" else t_nomod
+                    scases[f"d{Ds}_s{Ss}_{cname}"] = {
+                        "us": round(t * 1e6, 1), "tflops_dense_equiv": round(dense / t / 1e12, 1),
+                        "tflops_algorithmic": round(alg / t / 1e12, 1),
+                        "frac_bf16_peak": round(alg / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "latency_vs_no_mod": round(t / t_nomod, 3) if t_nomod else None}
+                del sq_, sk_, sv_, sout
 
     # ---- GQA cross-attention at its own shape: B2 Hq32 Hkv8 D128 Sq1024 Skv8192, bf16 and
     # f16, with the hash mask_mod that drops about 5% of the query rows, then also
@@ -478,19 +559,23 @@ def main():
                    "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
         "fwd_ms": round(float(fwd_ms.mean()), 4),
         "fwd_ms_std": round(float(fwd_ms.std()), 4),
+        "fwd_pages_method": {**fwd_pages, "tflops": round(flops / (fwd_pages["mean_us"] * 1e-6) / 1e12, 1)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_fwd, "kernel": FWD_KERNEL,
                      "algorithmic": f"{flops:.4e} flop per launch (4*B*H*S*S*D)"},
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s", "us": round(dec_avg_s * 1e6, 2),
+            "pages_method": {**dec_pages, "GBs": round(dbytes / (dec_pages["mean_us"] * 1e-6) / 1e9, 1)},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_dec,
                          "kernel": "+".join(DEC_KERNELS),
                          "algorithmic": f"{dbytes} bytes per call (K+V+mask+q+out+lse)"},
         },
         "cases_s8192": cases,
-        "cases_dense_short": ({"workload": "fwd bf16 B2 H32 D128 Sq=Skv in {2048, 4096} +LSE; causal half-counted",
+        "cases_dense_short": ({"workload": "fwd bf16 B2 H32 +LSE: D128 at Sq=Skv 2048 and 4096 with every flex "
+                                           "case, D64 at 2048 and 8192; causal half-counted, sliding window "
+                                           "over visited pairs",
                                **scases} if scases else {}),
         "cases_gqa_cross": {"workload": "fwd B2 Hq32 Hkv8 D128 Sq1024 Skv8192, ~5% of query rows dropped "
                                         "by a hash mask_mod; _window adds |i-j|<=256 AND j<=i (top-left)",
@@ -549,6 +634,60 @@ def main():
         dcases["contiguous_b8_h32_l32768"] = {"us": round(t * 1e6, 2), "GBs": round(cbytes / t / 1e9, 1),
                                               "bytes": cbytes}
         del ck, cv
+
+        # latency ladder of the pages' decode table: B1 H32 D128 f16 with the pad mask at
+        # KV lengths 1, 17, 1000 and 4096 (32768 is the headline call above). From 1000 on,
+        # enough input sets rotate that one pass over them exceeds the 256 MB Infinity
+        # Cache, so every call streams its K/V from HBM; below that the call is launch-bound.
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(17)
+        ladder = {}
+        for Ll in (1, 17, 1000, 4096):
+            per_set = dec_bytes(1, Hd, Ll, Dd)
+            nsets = -(-300_000_000 // per_set) if Ll >= 1000 else 1
+            sets = []
+            for r in range(nsets):
+                lk = torch.randn(1, Hd, Ll, Dd, device=dev, generator=gen).half()
+                lv = torch.randn(1, Hd, Ll, Dd, device=dev, generator=gen).half()
+                lq = torch.randn(1, Hd, 1, Dd, device=dev, generator=gen).half()
+                lm = torch.zeros(1, Hd, 1, Ll, device=dev, dtype=torch.float16)
+                pad = int(torch.randint(0, Ll, (1,), generator=gen, device=dev))
+                if pad:
+                    lm[..., Ll - pad:] = float("-inf")
+                sets.append((lq, lk, lv, lm))
+            lws = torch.empty(mm.decode_workspace_size(1, Hd, Ll, Dd) // 4 + 4, dtype=torch.float32, device=dev)
+            lout = torch.empty(1, Hd, 1, Dd, device=dev, dtype=torch.float16)
+            llse = torch.empty(1, Hd, device=dev, dtype=torch.float32)
+            lcall = [0]
+
+            def ladder_call():
+                lq, lk, lv, lm = sets[lcall[0] % nsets]
+                lcall[0] += 1
+                mm.attn_decode(lq, lk, lv, Ll, dscale, mask=lm, workspace=lws, out=lout, lse=llse)
+            st = pages_stats(torch, stream, ladder_call)
+            ladder[f"l{Ll}"] = {**st, "GBs": round(per_set / (st["mean_us"] * 1e-6) / 1e9, 1),
+                                "bytes": per_set, "rotation": f"{nsets} input sets, {nsets * per_set / 1e6:.0f} MB"}
+            del sets
+        ladder["l32768"] = {**dec_pages, "GBs": round(dbytes / (dec_pages["mean_us"] * 1e-6) / 1e9, 1),
+                            "bytes": dbytes, "rotation": f"1 input set of {dbytes / 1e6:.0f} MB"}
+        res["decode_latency"] = {"workload": "decode f16 B1 H32 D128 +pad mask +LSE at KV length L", **ladder}
+
+        # a batch of 8 sequences whose KV lengths are drawn from the ladder's lengths (cache
+        # capacity 32768, per-sequence lengths passed to the kernel)
+        Bm = 8
+        lens_m = np.random.default_rng(29).choice([1, 17, 1000, 4096, 32768], size=Bm)
+        mk = torch.randn(Bm, Hd, L, Dd, device=dev, generator=gen).half()
+        mv = torch.randn(Bm, Hd, L, Dd, device=dev, generator=gen).half()
+        mq = torch.randn(Bm, Hd, 1, Dd, device=dev, generator=gen).half()
+        mlens = torch.from_numpy(lens_m.astype(np.int32)).to(dev)
+        mws = torch.empty(mm.decode_workspace_size(Bm, Hd, L, Dd) // 4 + 4, dtype=torch.float32, device=dev)
+        kvmax = int(lens_m.max())
+        st = pages_stats(torch, stream, lambda: mm.attn_decode(mq, mk, mv, kvmax, dscale, seq_lens=mlens,
+                                                               workspace=mws))
+        mbytes = int(sum(Hd * int(n) * Dd * 2 * 2 for n in lens_m)) + 2 * Bm * Hd * Dd * 2 + Bm * Hd * 4 + Bm * 4
+        dcases["mixed_b8_h32"] = {**st, "GBs": round(mbytes / (st["mean_us"] * 1e-6) / 1e9, 1), "bytes": mbytes,
+                                  "lens": [int(n) for n in lens_m], "Scap": L}
+        del mk, mv
         res["decode_cases"] = dcases
 
     # backward (bf16, same shape): dq, dk, dv of sum(dO * O) from the forward's O and LSE
@@ -600,7 +739,7 @@ def main():
                          "algorithmic": "4*B*H*S*S*D flop per launch; e4m3 Q/K/V, bf16 O"},
         }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(xf, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(xf, args.cpu_seconds, xd=xd)
     print(json.dumps(res), flush=True)
 
 
