@@ -233,7 +233,8 @@ size_t mm_attn_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Sq);
 mm_status mm_attn_bwd(const mm_bwd_args *args, void *stream);
 
 /* Bytes of device workspace mm_attn_decode needs for these sizes (0 if invalid).
- * num_splits as in mm_decode_args (0 = automatic). */
+ * num_splits as in mm_decode_args (0 = automatic). Sized for the larger automatic
+ * split count of a call with seq_lens, so it serves calls with and without them. */
 size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t D,
                                      int32_t num_splits);
 
@@ -278,6 +279,15 @@ mm_status mm_attn_decode_noalloc(const mm_decode_args *args, void *stream);
  * whole number of the split loop's iterations, so the last splits of a row may be
  * empty (they contribute nothing; the workspace size does not change). */
 int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len);
+
+/* Split count mm_attn_decode uses when num_splits == 0 and seq_lens is given. The
+ * lengths are then known only on the device and one sequence may hold nearly all the
+ * keys, so the count of mm_attn_decode_auto_splits is raised to the one a batch of a
+ * single sequence would get, as far as the split workgroups stay within 8 resident
+ * rounds (8192 with one query head per workgroup, 4096 with 2 or 4); the same bounds
+ * and rounding apply. Splits past a sequence's length end at once and weigh nothing in
+ * the merge. Equal to mm_attn_decode_auto_splits for B = 1. 0 if the sizes are invalid. */
+int32_t mm_attn_decode_auto_splits_varlen(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len);
 
 /* Block-mask classes of the built-in mask_mods, the analogue of building a BlockMask
  * from a mask_mod: out[qb*ld + kb] (device bytes, qb < ceil(Sq/MM_BLOCK_Q),

@@ -150,6 +150,8 @@ def load_library():
     lib.mm_attn_decode_workspace_size.argtypes = [ctypes.c_int32] * 6
     lib.mm_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.mm_attn_decode_auto_splits.argtypes = [ctypes.c_int32] * 4
+    lib.mm_attn_decode_auto_splits_varlen.argtypes = [ctypes.c_int32] * 4
+    lib.mm_attn_decode_auto_splits_varlen.restype = ctypes.c_int32
     lib.mm_attn_decode_auto_splits.restype = ctypes.c_int32
     lib.mm_block_mask_create.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
@@ -425,9 +427,12 @@ def decode_workspace_size(B, Hq, kv_len, D, num_splits=0, Hkv=None) -> int:
     return int(load_library().mm_attn_decode_workspace_size(B, Hq, Hkv, kv_len, D, num_splits))
 
 
-def decode_auto_splits(B, Hq, kv_len, Hkv=None) -> int:
+def decode_auto_splits(B, Hq, kv_len, Hkv=None, varlen=False) -> int:
+    """Automatic split count of attn_decode; varlen: for a call with seq_lens."""
     Hkv = Hq if Hkv is None else Hkv
-    return int(load_library().mm_attn_decode_auto_splits(B, Hq, Hkv, kv_len))
+    lib = load_library()
+    fn = lib.mm_attn_decode_auto_splits_varlen if varlen else lib.mm_attn_decode_auto_splits
+    return int(fn(B, Hq, Hkv, kv_len))
 
 
 def attn_decode_noalloc(q, k_cache, v_cache, kv_len, scale, *, mask=None, seq_lens=None,

@@ -50,6 +50,7 @@ void *scratch_address(hipStream_t stream) {
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
 constexpr int kTargetDecodeBlocks = 1024;  // ~4 workgroups per CU, one resident round
+constexpr int kVarlenGridFactor = 8;       // with per-sequence lengths: at most 8 rounds
 // Sequence lengths stay below 2^30 so that the kernels' 32-bit index arithmetic (a row
 // plus the window plus one, a key tile's end) cannot overflow.
 constexpr int32_t kMaxSeq = 1 << 30;
@@ -102,14 +103,24 @@ int decode_heads_per_wg(int32_t Hq, int32_t Hkv) {
 // split shorter than kMinKeysPerSplit keys; and, when a kv head's group spans several
 // workgroups, a multiple of 8: workgroups are placed on the 8 XCDs round-robin by
 // linear id (split fastest), so the workgroups that read the same K/V chunk then share
-// one XCD's L2 instead of each fetching it from HBM
-int decode_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t requested) {
+// one XCD's L2 instead of each fetching it from HBM.
+// varlen (per-sequence lengths, known only on the device): one sequence may hold
+// nearly all of the batch's keys, so the count is raised to what a batch of one would
+// get, within a grid of kVarlenGridFactor resident rounds; the workgroups of the
+// shorter sequences' empty splits end at once.
+int decode_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t requested, bool varlen) {
     if (requested > 0) return requested;
     if (kv_len <= 0) return 1;
     const int G = decode_heads_per_wg(Hq, Hkv);
     const int64_t rows = (int64_t)B * Hq / G;
     const int64_t target = G > 1 ? kTargetDecodeBlocks / 2 : kTargetDecodeBlocks;
     int64_t want = target / rows;
+    if (varlen) {
+        const int64_t one = target / (Hq / G);
+        const int64_t cap = kVarlenGridFactor * target / rows;
+        const int64_t raised = one < cap ? one : cap;
+        if (raised > want) want = raised;
+    }
     const int64_t by_len = ((int64_t)kv_len + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
     if (want > by_len) want = by_len;
     if (want > kMaxSplits) want = kMaxSplits;
@@ -353,7 +364,12 @@ mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
 
 int32_t mm_attn_decode_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || kv_len < 0) return 0;
-    return decode_splits(B, Hq, Hkv, kv_len, 0);
+    return decode_splits(B, Hq, Hkv, kv_len, 0, false);
+}
+
+int32_t mm_attn_decode_auto_splits_varlen(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || kv_len < 0) return 0;
+    return decode_splits(B, Hq, Hkv, kv_len, 0, true);
 }
 
 size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t D,
@@ -361,7 +377,7 @@ size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || kv_len < 0 || (D != 64 && D != 128) ||
         num_splits < 0 || num_splits > kMaxSplits)
         return 0;
-    const int splits = decode_splits(B, Hq, Hkv, kv_len, num_splits);
+    const int splits = decode_splits(B, Hq, Hkv, kv_len, num_splits, true);  // >= the count without seq_lens
     return (size_t)B * Hq * splits * (size_t)(D + 2) * sizeof(float);
 }
 
@@ -398,7 +414,7 @@ mm_status decode_impl(const mm_decode_args *a, void *stream, bool static_scratch
     }
     if (a->B == 0) return MM_OK;
 
-    const int splits = decode_splits(a->B, a->Hq, a->Hkv, a->kv_len, a->num_splits);
+    const int splits = decode_splits(a->B, a->Hq, a->Hkv, a->kv_len, a->num_splits, a->seq_lens != nullptr);
     const size_t need = (size_t)a->B * a->Hq * splits * (size_t)(a->D + 2) * sizeof(float);
     void *workspace = a->workspace;
     size_t workspace_bytes = a->workspace_bytes;

@@ -76,17 +76,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     __shared__ float sm_m[SLOTS], sm_l[SLOTS];
     __shared__ __attribute__((aligned(16))) float sm_o[SLOTS][D];
 
-    const int s = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+    const int hg = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / LPK, c = lane % LPK;
     const int slot = wave * KPW + g;
     const int h0 = hg * G;           // first query head of this workgroup
     const int hk = h0 / p.group;     // G divides the group: one kv head for all G
+    // Workgroups go to the 8 XCDs round-robin by linear id, split index fastest. The
+    // split index is rotated by the (batch, kv head) index, so that the first splits of
+    // the rows (the only non-empty ones of a short sequence) spread over the XCDs
+    // instead of all landing on one; the workgroups of one kv head keep the same
+    // rotation, so those that read the same chunk still share an XCD.
+    const int s = (int)(((int64_t)blockIdx.x + (int64_t)b * p.Hkv + hk) % p.splits);
 
     int len = p.kv_len;
     if (p.lens) len = min(max(p.lens[b], 0), p.kv_len);
     const int j_begin = s * p.chunk;
     const int j_end = min(len, j_begin + p.chunk);
+    if (j_begin >= j_end) {
+        // an empty split (a short sequence, or the rounded-up tail): weight 0 in the
+        // merge, which then reads neither its output partial nor anything else of it
+        if (tid < G) {
+            const int64_t wi = ((int64_t)b * p.Hq + h0 + tid) * p.splits + s;
+            p.ws_m[wi] = -INFINITY;
+            p.ws_l[wi] = 0.f;
+        }
+        return;
+    }
 
     u32x4 qv[G];
 #pragma unroll
@@ -115,9 +131,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
         o[gi] = f32x8{};
     }
 
-    for (int base = j_begin; base < j_end; base += STEP * U) {
-        u32x4 kr[U], vr[U];
-        uint16_t mk[U][G];
+    // one iteration's loads: K/V rows of its U steps (and the G heads' mask entries);
+    // then the page table entries of the next iteration
+    auto load_iter = [&](int base, u32x4 (&kr)[U], u32x4 (&vr)[U], uint16_t (&mk)[U][G])
+        __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = min(base + u * STEP + slot, j_end - 1);  // tail lanes re-read a valid key
@@ -134,6 +151,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
 #pragma unroll
             for (int u = 0; u < U; ++u) pg[u] = bt[min(base + STEP * U + u * STEP + slot, j_end - 1) >> p.page_shift];
         }
+    };
+    // online softmax over one iteration's keys for each of the G heads
+    auto consume = [&](int base, const u32x4 (&kr)[U], const u32x4 (&vr)[U], const uint16_t (&mk)[U][G])
+        __attribute__((always_inline)) {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             float t[U];
@@ -159,6 +180,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
             }
             m[gi] = m_new;
         }
+    };
+
+    for (int base = j_begin; base < j_end; base += STEP * U) {
+        u32x4 kr[U], vr[U];
+        uint16_t mk[U][G];
+        load_iter(base, kr, vr, mk);
+        consume(base, kr, vr, mk);
     }
 
     // combine the SLOTS partial states of each head (one head at a time through LDS)
@@ -230,11 +258,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     const float *op0 = p.ws_o + w0 * D + d;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int s0 = sg;
+    // a split of weight 0 (empty, or every key masked) is not read: an empty split
+    // leaves its output partial unwritten. The weight test is uniform over each wave
+    // (a wave's lanes share sg), so skipped loads cost no memory traffic.
     for (; s0 + 7 * SG < S; s0 += 8 * SG) {  // 8 independent loads in flight
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = fmaf(sm_w[s0 + u * SG], op0[(int64_t)(s0 + u * SG) * D], acc[u]);
+        for (int u = 0; u < 8; ++u) {
+            const float wu = sm_w[s0 + u * SG];
+            const float ou = wu != 0.f ? op0[(int64_t)(s0 + u * SG) * D] : 0.f;
+            acc[u] = fmaf(wu, ou, acc[u]);
+        }
     }
-    for (; s0 < S; s0 += SG) acc[0] = fmaf(sm_w[s0], op0[(int64_t)s0 * D], acc[0]);
+    for (; s0 < S; s0 += SG) {
+        const float wu = sm_w[s0];
+        acc[0] = fmaf(wu, wu != 0.f ? op0[(int64_t)s0 * D] : 0.f, acc[0]);
+    }
     sm_acc[sg][d] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     __syncthreads();
     if (tid < D) {

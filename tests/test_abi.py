@@ -292,6 +292,37 @@ def test_bwd_workspace_size():
     assert mm.bwd_workspace_size(1, 1, 0) == 0
 
 
+def test_decode_varlen_splits():
+    """With per-sequence lengths the automatic split count is raised towards what a batch
+    of one sequence gets (one sequence may hold nearly all the keys), keeping the split
+    workgroups within 8 resident rounds; the workspace size covers that count."""
+    assert mm.decode_auto_splits(8, 32, 32768, varlen=True) == 32      # as B = 1: 1024 / 32
+    assert mm.decode_auto_splits(8, 32, 32768) == 4
+    assert mm.decode_workspace_size(8, 32, 32768, 128) == 8 * 32 * 32 * 130 * 4
+    assert mm.decode_auto_splits(64, 32, 32768, varlen=True) == 4      # 8192 / 2048 rows
+    assert mm.decode_auto_splits(8, 32, 32768, Hkv=8, varlen=True) == 64  # G 4: 512 / 8, 4096 / 64 rows
+    assert mm.load_library().mm_attn_decode_auto_splits_varlen(1, 32, 5, 100) == 0
+    for B in (1, 2, 3, 8, 64, 1000):
+        for Hq, Hkv in ((32, 32), (32, 8), (32, 4), (24, 8), (7, 1)):
+            for L in (1, 255, 1000, 32768, 262144):
+                s0 = mm.decode_auto_splits(B, Hq, L, Hkv=Hkv)
+                s1 = mm.decode_auto_splits(B, Hq, L, Hkv=Hkv, varlen=True)
+                group = Hq // Hkv
+                G = next(g for g in (4, 2, 1) if group % g == 0)
+                assert s1 >= s0 and 1 <= s1 <= min(256, -(-L // 256)), (B, Hq, Hkv, L, s0, s1)
+                if B == 1:
+                    assert s1 == s0
+                if s1 > s0:
+                    assert (B * Hq // G) * s1 <= 8 * (1024 if G == 1 else 512)
+                if group > G and s1 >= 8:
+                    assert s1 % 8 == 0
+                for D in (64, 128):
+                    assert mm.decode_workspace_size(B, Hq, L, D, Hkv=Hkv) == B * Hq * s1 * (D + 2) * 4
+                    # the raised count never pushes a call past the static scratch
+                    if B * Hq * s0 * (D + 2) * 4 <= mm.DECODE_SCRATCH_BYTES:
+                        assert B * Hq * s1 * (D + 2) * 4 <= mm.DECODE_SCRATCH_BYTES
+
+
 def test_decode_noalloc_rejects_oversize_before_any_device_work():
     """mm_attn_decode_noalloc refuses, before touching a device, a call whose partials
     exceed the static scratch; calls with nothing to do return OK."""

@@ -13,7 +13,7 @@ LENGTHS = [1, 17, 1000, 4096, 32768]
 
 
 def _run(B, Hq, Hkv, lens, D, dtype, *, Scap=None, kv_len=None, use_mask=True, use_lens=True,
-         bias_seed=None, seed=0, num_splits=0, scale=SCALE, mask_override=None):
+         bias_seed=None, seed=0, num_splits=0, scale=SCALE, mask_override=None, nan_workspace=False):
     import torch
     import mask_mods_amd as mm
     lens = np.asarray(lens, dtype=np.int64)
@@ -37,7 +37,13 @@ def _run(B, Hq, Hkv, lens, D, dtype, *, Scap=None, kv_len=None, use_mask=True, u
             mask_bits = mask_override(mask_bits)
     mask = to_torch(mask_bits, "f16") if mask_bits is not None else None
     seq = torch.tensor(x["lens"], dtype=torch.int32, device="cuda") if use_lens else None
-    out, lse = mm.attn_decode(q, k, v, kv_len, scale, mask=mask, seq_lens=seq, num_splits=num_splits)
+    ws = None
+    if nan_workspace:
+        # every partial the kernels do not write stays NaN: reading one shows in O
+        need = mm.decode_workspace_size(B, Hq, kv_len, D, num_splits=num_splits, Hkv=Hkv)
+        ws = torch.full(((need + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    out, lse = mm.attn_decode(q, k, v, kv_len, scale, mask=mask, seq_lens=seq, num_splits=num_splits,
+                              workspace=ws)
     torch.cuda.synchronize()
     qd, kd, vd = (inputs.bits_to_f64(x[n], dtype) for n in ("q", "k", "v"))
     md = inputs.bits_to_f64(mask_bits, "f16") if mask_bits is not None else None
@@ -62,6 +68,16 @@ def test_config_decode_b8_per_sequence_lengths():
     lens = g.choice(LENGTHS, size=8)
     lens[0] = 32768
     _run(8, 32, 32, lens, 128, "f16", Scap=32768, seed=1)
+
+
+@pytest.mark.parametrize("Hkv,use_mask", [(32, True), (32, False), (8, True), (4, False)])
+def test_varlen_empty_splits_are_not_read(Hkv, use_mask):
+    """With per-sequence lengths the split count is raised for the longest possible
+    sequence, so most splits of the short ones are empty: they write only their (max,
+    sum), and the merge must not read their output partials. The workspace starts as
+    NaN, so any such read would show in O."""
+    _run(8, 32, Hkv, [4096, 1, 0, 17, 1000, 300, 4096, 2], 128, "f16", Scap=4096, seed=21,
+         use_mask=use_mask, nan_workspace=True)
 
 
 def test_finite_bias_mask_added_after_scale():
