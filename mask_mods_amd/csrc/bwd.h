@@ -69,12 +69,11 @@ void bwd_dq_kernel(BwdParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt_idx = L % p.n_tiles;
-    L /= p.n_tiles;
-    const int h = L % p.Hq;
-    const int b = L / p.Hq;
-    const int qt = (MASK & MASK_CAUSAL) ? (p.n_tiles - 1 - qt_idx) : qt_idx;
+    // causal: the last query tiles carry the most keys; they start first
+    int qt, pair;
+    work_item(blockIdx.x, gridDim.x, p.n_tiles, (MASK & MASK_CAUSAL) != 0, qt, pair);
+    const int h = pair % p.Hq;
+    const int b = pair / p.Hq;
     const int q0 = qt * BM;
     const int hk = h / p.group;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -349,11 +348,12 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int kt = L % p.n_tiles;
-    L /= p.n_tiles;
-    const int hk = L % p.Hkv;
-    const int b = L / p.Hkv;
+    // causal: the first key tiles are seen by the most queries; they start first
+    int kt, pair;
+    work_item(blockIdx.x, gridDim.x, p.n_tiles, (MASK & MASK_CAUSAL) != 0, kt, pair);
+    if (MASK & MASK_CAUSAL) kt = p.n_tiles - 1 - kt;
+    const int hk = pair % p.Hkv;
+    const int b = pair / p.Hkv;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int kw0 = kt * BNK + wave_s * 32;  // this wave's first key
     const int key = kw0 + l32;               // the key this lane owns

@@ -89,6 +89,25 @@ __device__ __forceinline__ int xcd_remap(int p, int n) {
     return x * q + (x < r ? x : r) + s;
 }
 
+// Work item of workgroup p of n = n_tiles * pairs (pairs = (batch, head) rows): its tile
+// index and its pair. Plain: the XCD remap above, tiles fastest, so all the tiles of a
+// pair share one XCD's L2. Causal (heavy = true: tile t carries about t + 1 units of
+// work): tile-major over the whole grid, heaviest tiles first, so that the dispatcher
+// starts every pair's longest tile before any shorter one and the short tiles fill in
+// at the end (longest-first list scheduling); workgroups go to the XCDs round-robin by
+// id, so with pairs a multiple of 8 a pair's tiles still share an XCD.
+__device__ __forceinline__ void work_item(int p, int n, int n_tiles, bool heavy_last, int &tile, int &pair) {
+    if (heavy_last) {
+        const int pairs = n / n_tiles;
+        tile = n_tiles - 1 - p / pairs;
+        pair = p % pairs;
+    } else {
+        const int L = xcd_remap(p, n);
+        tile = L % n_tiles;
+        pair = L / n_tiles;
+    }
+}
+
 // On a non-decreasing int32 array of n entries: the first index whose value is >= v
 // (lower) or > v (upper); n if none.
 __device__ __forceinline__ int doc_lower(const int32_t *a, int n, int v) {

@@ -79,12 +79,11 @@ void fwd_fp8_kernel(FwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
 
-    int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt_idx = L % p.n_qtiles;
-    L /= p.n_qtiles;
-    const int h = L % p.Hq;
-    const int b = L / p.Hq;
-    const int qt = (MASK & MASK_CAUSAL) ? (p.n_qtiles - 1 - qt_idx) : qt_idx;
+    // causal: the last query tiles carry the most keys; they start first
+    int qt, pair;
+    work_item(blockIdx.x, gridDim.x, p.n_qtiles, (MASK & MASK_CAUSAL) != 0, qt, pair);
+    const int h = pair % p.Hq;
+    const int b = pair / p.Hq;
     const int q0 = qt * BM;
     const int hk = h / p.group;
 

@@ -67,13 +67,11 @@ void fwd_mfma_kernel(FwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
 
-    int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt_idx = L % p.n_qtiles;
-    L /= p.n_qtiles;
-    const int h = L % p.Hq;
-    const int b = L / p.Hq;
-    // causal: the last query tiles carry the most keys; start them first
-    const int qt = (MASK & MASK_CAUSAL) ? (p.n_qtiles - 1 - qt_idx) : qt_idx;
+    // causal: the last query tiles carry the most keys; they start first
+    int qt, pair;
+    work_item(blockIdx.x, gridDim.x, p.n_qtiles, (MASK & MASK_CAUSAL) != 0, qt, pair);
+    const int h = pair % p.Hq;
+    const int b = pair / p.Hq;
     const int q0 = qt * BM;
     const int hk = h / p.group;
 
@@ -287,6 +285,23 @@ void fwd_mfma_kernel(FwdParams p) {
             // carries no per-score compare and select. Without alibi a general tile
             // nearly always needs the predicates (and they keep every pair of a tile
             // that does not), so only the masked copy is emitted.
+            // Every predicate keeps an interval of keys (j < Skv; causal j <= row; window
+            // |row - j| <= w; the document's keys [dfirst, dend)), so the lane's kept keys
+            // in this tile are one interval of the offsets jo = j - k0 - 4*hi: [jlo, jlo +
+            // span). Each score then costs one subtraction and one unsigned compare. The
+            // host keeps Sq, Skv < 2^30 and the window <= max(Sq, Skv), so no bound overflows.
+            const int rel = row - k0 - 4 * hi;  // the row as an offset jo
+            int jlo = 0, jhi = p.Skv - k0 - 4 * hi;
+            if ((MASK & MASK_CAUSAL) && pred) jhi = min(jhi, rel + 1);
+            if ((MASK & MASK_WINDOW) && pred) {
+                jlo = max(jlo, rel - p.window);
+                jhi = min(jhi, rel + p.window + 1);
+            }
+            if ((MASK & MASK_DOC) && pred) {
+                jlo = max(jlo, dfirst - 4 * hi);
+                jhi = min(jhi, dend - 4 * hi);
+            }
+            const uint32_t span = jhi > jlo ? (uint32_t)(jhi - jlo) : 0u;
             auto scores = [&](bool masked) __attribute__((always_inline)) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
@@ -294,14 +309,7 @@ void fwd_mfma_kernel(FwdParams p) {
                     for (int e = 0; e < 16; ++e) {
                         const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
                         float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
-                        if (masked) {
-                            const int j = k0 + 4 * hi + jo;
-                            bool keep = j < p.Skv;
-                            if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
-                            if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                            if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
-                            t = keep ? t : -INFINITY;
-                        }
+                        if (masked) t = (uint32_t)(jo - jlo) < span ? t : -INFINITY;
                         sacc[kb][e] = t;
                         mloc = fmaxf(mloc, t);
                     }
