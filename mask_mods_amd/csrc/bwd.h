@@ -226,6 +226,20 @@ void bwd_dq_kernel(BwdParams p) {
             uint32_t dsp[8];
             // gen: scale and alibi applied to the score; masked: the predicates too (an
             // alibi tile that needs no mask takes gen without masked)
+            // the lane's kept keys in this 32-key block: one interval of offsets jo = j -
+            // k0 - 4*hi (each predicate keeps an interval)
+            const int rel = row - k0 - 4 * hi;
+            int jlo = 0, jhi = p.Skv - k0 - 4 * hi;
+            if ((MASK & MASK_CAUSAL) && pred) jhi = min(jhi, rel + 1);
+            if ((MASK & MASK_WINDOW) && pred) {
+                jlo = max(jlo, rel - p.window);
+                jhi = min(jhi, rel + p.window + 1);
+            }
+            if ((MASK & MASK_DOC) && pred) {
+                jlo = max(jlo, dfirst - 4 * hi);
+                jhi = min(jhi, dend - 4 * hi);
+            }
+            const uint32_t span = jhi > jlo ? (uint32_t)(jhi - jlo) : 0u;
             auto make_ds = [&](bool gen, bool masked) {
                 const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
 #pragma unroll
@@ -238,14 +252,7 @@ void bwd_dq_kernel(BwdParams p) {
                         float pv;
                         if (gen) {
                             const float t = ALIBI ? fmaf(sacc[e], c2, fmaf(slope2, (float)jo, base)) : sacc[e] * c2;
-                            bool keep = true;
-                            if (masked) {
-                                const int j = k0 + 4 * hi + jo;
-                                keep = j < p.Skv;
-                                if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
-                                if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                                if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
-                            }
+                            const bool keep = !masked || (uint32_t)(jo - jlo) < span;
                             pv = keep ? fast_exp2(t - lse2) : 0.f;
                         } else {
                             pv = fast_exp2(fmaf(sacc[e], c2, -lse2));
@@ -540,6 +547,23 @@ void bwd_dkdv_kernel(BwdParams p) {
         uint32_t pp[RB][8], dsp[RB][8];
         // general: scale and alibi applied to the score; masked: the predicates too
         auto make = [&](bool general, bool masked) {
+            // the lane's kept rows in this tile: one interval of offsets io = i - i0 -
+            // 4*hi (each predicate keeps an interval; a key past Skv keeps none)
+            int ilo = 0, ihi = 0;
+            if (masked) {
+                const int relk = key - i0 - 4 * hi;
+                ihi = key_ok ? p.Sq - i0 - 4 * hi : 0;
+                if ((MASK & MASK_CAUSAL) && pred) ilo = max(ilo, relk);
+                if ((MASK & MASK_WINDOW) && pred) {
+                    ilo = max(ilo, relk - p.window);
+                    ihi = min(ihi, relk + p.window + 1);
+                }
+                if ((MASK & MASK_DOC) && pred) {
+                    ilo = max(ilo, dfirst - 4 * hi);
+                    ihi = min(ihi, dend - 4 * hi);
+                }
+            }
+            const uint32_t span = ihi > ilo ? (uint32_t)(ihi - ilo) : 0u;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -551,15 +575,10 @@ void bwd_dkdv_kernel(BwdParams p) {
                         const float lse2 = l2[rb][e >> 2][e & 3];
                         float x;
                         if (general) {
-                            const int i = i0 + 32 * rb + 4 * hi + 8 * (e >> 2) + (e & 3);
+                            const int io = 32 * rb + 8 * (e >> 2) + (e & 3);
+                            const int i = i0 + 4 * hi + io;
                             const float t = ALIBI ? fmaf(sacc[rb][e], c2, slope2 * (float)(key - i)) : sacc[rb][e] * c2;
-                            bool keep = true;
-                            if (masked) {
-                                keep = key_ok && i < p.Sq;
-                                if ((MASK & MASK_CAUSAL) && pred) keep &= key <= i;
-                                if ((MASK & MASK_WINDOW) && pred) keep &= abs(i - key) <= p.window;
-                                if ((MASK & MASK_DOC) && pred) keep &= i - i0 >= dfirst && i - i0 < dend;
-                            }
+                            const bool keep = !masked || (uint32_t)(io - ilo) < span;
                             x = keep ? fast_exp2(t - lse2) : 0.f;
                             ds[u] = keep ? x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]) : 0.f;
                         } else {

@@ -251,6 +251,20 @@ void fwd_fp8_kernel(FwdParams p) {
         int dfirst = 0, dend = BN;
         if ((MASK & MASK_DOC) && doc_mask)
             tile_doc_range(p.kvdoc[b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1)], mydoc, dfirst, dend);
+        // the lane's kept keys in the tile: one interval of offsets jo = j - k0 - 4*hi
+        // (each predicate keeps an interval; a dead tile keeps none)
+        const int rel = row - k0 - 4 * hi;
+        int jlo = 0, jhi = dead ? 0 : p.Skv - k0 - 4 * hi;
+        if ((MASK & MASK_CAUSAL) && pred) jhi = min(jhi, rel + 1);
+        if ((MASK & MASK_WINDOW) && pred) {
+            jlo = max(jlo, rel - p.window);
+            jhi = min(jhi, rel + p.window + 1);
+        }
+        if ((MASK & MASK_DOC) && pred) {
+            jlo = max(jlo, dfirst - 4 * hi);
+            jhi = min(jhi, dend - 4 * hi);
+        }
+        const uint32_t span = jhi > jlo ? (uint32_t)(jhi - jlo) : 0u;
         auto scores = [&](bool masked) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -258,14 +272,7 @@ void fwd_fp8_kernel(FwdParams p) {
                 for (int e = 0; e < 16; ++e) {
                     const int jo = 32 * kb + 8 * (e >> 2) + (e & 3);
                     float t = ALIBI ? fmaf(sacc[kb][e], c2, fmaf(slope2, (float)jo, base)) : sacc[kb][e] * c2;
-                    if (masked) {
-                        const int j = k0 + 4 * hi + jo;
-                        bool keep = (j < p.Skv) & !dead;
-                        if ((MASK & MASK_CAUSAL) && pred) keep &= j <= row;
-                        if ((MASK & MASK_WINDOW) && pred) keep &= abs(row - j) <= p.window;
-                        if ((MASK & MASK_DOC) && pred) keep &= j - k0 >= dfirst && j - k0 < dend;
-                        t = keep ? t : -INFINITY;
-                    }
+                    if (masked) t = (uint32_t)(jo - jlo) < span ? t : -INFINITY;
                     sacc[kb][e] = t;
                 }
             }
