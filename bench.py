@@ -246,6 +246,45 @@ def pages_stats(torch, stream, fn):
             "method": f"{PAGES_WARMUP} warmup, {PAGES_SAMPLES} samples x {PAGES_ITERS} calls"}
 
 
+def graph_stats(torch, dev, call, snapshot, last_set, eager):
+    """The pages' method on a captured HIP graph of PAGES_ITERS calls (no host launch cost
+    in the timed region): PAGES_SAMPLES replays after a warmup replay. Each replay's last
+    output is checked against an eager call on the same inputs (bitwise: the kernels are
+    deterministic); the replays alternate with that eager work and synchronisations."""
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(PAGES_ITERS):
+            call()
+    torch.cuda.synchronize()
+    st = last_set()  # the inputs of the graph's last call
+    stream = torch.cuda.current_stream(dev)
+    us, ok = [], True
+    for i in range(PAGES_SAMPLES + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        o_g, l_g = snapshot()
+        o_e, l_e = eager(st)
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(o_g, o_e)) and bool(torch.equal(l_g, l_e))
+        if i > 0:
+            us.append(e0.elapsed_time(e1) / PAGES_ITERS * 1e3)
+    del g
+    us = np.array(us)
+    return {"mean_us": round(float(us.mean()), 2), "std_us": round(float(us.std()), 2),
+            "cv_pct": round(float(us.std() / us.mean() * 100), 2),
+            "method": f"HIP graph of {PAGES_ITERS} calls, {PAGES_SAMPLES} replays after one warmup replay",
+            "replays_equal_eager": ok}
+
+
 def profile_one(args, torch, mm, inputs, dev):
     """Run one kernel family only (for rocprofv3 passes); prints a small JSON line."""
     def dev_tensor(bits, dtype):
@@ -665,11 +704,18 @@ def main():
                 lcall[0] += 1
                 mm.attn_decode(lq, lk, lv, Ll, dscale, mask=lm, workspace=lws, out=lout, lse=llse)
             st = pages_stats(torch, stream, ladder_call)
-            ladder[f"l{Ll}"] = {**st, "GBs": round(per_set / (st["mean_us"] * 1e-6) / 1e9, 1),
-                                "bytes": per_set, "rotation": f"{nsets} input sets, {nsets * per_set / 1e6:.0f} MB"}
+            ent = {**st, "GBs": round(per_set / (st["mean_us"] * 1e-6) / 1e9, 1),
+                   "bytes": per_set, "rotation": f"{nsets} input sets, {nsets * per_set / 1e6:.0f} MB"}
+            ent["graph"] = graph_stats(torch, dev, ladder_call, lambda: (lout.clone(), llse.clone()),
+                                       lambda: (sets[(lcall[0] - 1) % nsets]),
+                                       lambda st_: mm.attn_decode(*st_[:3], Ll, dscale, mask=st_[3], workspace=lws))
+            ladder[f"l{Ll}"] = ent
             del sets
         ladder["l32768"] = {**dec_pages, "GBs": round(dbytes / (dec_pages["mean_us"] * 1e-6) / 1e9, 1),
                             "bytes": dbytes, "rotation": f"1 input set of {dbytes / 1e6:.0f} MB"}
+        ladder["l32768"]["graph"] = graph_stats(
+            torch, dev, dec, lambda: (dout.clone(), dlse.clone()), lambda: None,
+            lambda _: mm.attn_decode(dq, dk, dv, L, dscale, mask=dmask, workspace=ws))
         res["decode_latency"] = {"workload": "decode f16 B1 H32 D128 +pad mask +LSE at KV length L", **ladder}
 
         # a batch of 8 sequences whose KV lengths are drawn from the ladder's lengths (cache

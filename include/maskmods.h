@@ -238,7 +238,8 @@ mm_status mm_attn_bwd(const mm_bwd_args *args, void *stream);
 size_t mm_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t kv_len, int32_t D,
                                      int32_t num_splits);
 
-/* Decode attention (two launches on `stream`: split pass, then merge). With GQA
+/* Decode attention (two launches on `stream`: split pass, then merge; one launch when
+ * the split count is 1, the split pass then writing the output itself). With GQA
  * (Hq > Hkv) one workgroup of the split pass serves up to 4 query heads of a kv head,
  * so K/V are streamed once per 4 query heads (larger groups take several workgroups,
  * which the automatic split count places on one XCD so that they share its L2).
@@ -269,7 +270,7 @@ mm_status mm_attn_decode(const mm_decode_args *args, void *stream);
  *     partials (each call writes every partial it reads, so nothing needs clearing).
  *     Calls that overlap in time on one GPU (on different streams, or from threads
  *     without ordering) race and give undefined results: order them, e.g. on one stream.
- * Other rejections as mm_attn_decode. Two launches on `stream`. */
+ * Other rejections as mm_attn_decode. Launches as mm_attn_decode. */
 mm_status mm_attn_decode_noalloc(const mm_decode_args *args, void *stream);
 
 /* Split count mm_attn_decode uses when num_splits == 0: about one resident round of

@@ -95,8 +95,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     const int j_end = min(len, j_begin + p.chunk);
     if (j_begin >= j_end) {
         // an empty split (a short sequence, or the rounded-up tail): weight 0 in the
-        // merge, which then reads neither its output partial nor anything else of it
-        if (tid < G) {
+        // merge, which then reads neither its output partial nor anything else of it.
+        // With one split the row is empty: O = 0, LSE = -inf, written here.
+        if (p.splits == 1) {
+            for (int i = tid; i < G * D; i += 256) {
+                const int gi = i / D, d = i % D;
+                ((uint16_t *)p.o + b * p.o_sb + (h0 + gi) * p.o_sh)[d] = narrow1(0.f, TT{});
+                if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h0 + gi] = -INFINITY;
+            }
+        } else if (tid < G) {
             const int64_t wi = ((int64_t)b * p.Hq + h0 + tid) * p.splits + s;
             p.ws_m[wi] = -INFINITY;
             p.ws_l[wi] = 0.f;
@@ -214,11 +221,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
                     Od += sm_o[k][tid] * w;
                 }
             }
-            const int64_t wi = ((int64_t)b * p.Hq + h0 + gi) * p.splits + s;
-            p.ws_o[wi * D + tid] = Od;
-            if (tid == 0) {
-                p.ws_m[wi] = M;
-                p.ws_l[wi] = Ls;
+            if (p.splits == 1) {
+                // one split: this is the whole row; normalise here as the merge would
+                // (its weights are then exactly 1), and skip the merge launch
+                const bool live = Ls > 0.f;
+                ((uint16_t *)p.o + b * p.o_sb + (h0 + gi) * p.o_sh)[tid] = narrow1(live ? Od / Ls : 0.f, TT{});
+                if (tid == 0 && p.lse)
+                    p.lse[(int64_t)b * p.Hq + h0 + gi] = live ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+            } else {
+                const int64_t wi = ((int64_t)b * p.Hq + h0 + gi) * p.splits + s;
+                p.ws_o[wi * D + tid] = Od;
+                if (tid == 0) {
+                    p.ws_m[wi] = M;
+                    p.ws_l[wi] = Ls;
+                }
             }
         }
     }
@@ -305,7 +321,7 @@ static hipError_t launch_decode_t(const DecParams &p, hipStream_t s) {
         case 2: e = paged ? launch_split<TT, D, 2, true>(p, s) : launch_split<TT, D, 2, false>(p, s); break;
         default: e = paged ? launch_split<TT, D, 1, true>(p, s) : launch_split<TT, D, 1, false>(p, s); break;
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || p.splits == 1) return e;  // one split writes the output itself
     decode_merge_kernel<TT, D><<<dim3((unsigned)p.Hq, (unsigned)p.B), dim3(256), 0, s>>>(p);
     return hipGetLastError();
 }

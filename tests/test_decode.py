@@ -80,6 +80,14 @@ def test_varlen_empty_splits_are_not_read(Hkv, use_mask):
          use_mask=use_mask, nan_workspace=True)
 
 
+@pytest.mark.parametrize("Hkv,D,dtype", [(32, 128, "f16"), (8, 128, "bf16"), (4, 64, "f16"), (16, 64, "bf16")])
+def test_one_split_writes_the_output_itself(Hkv, D, dtype):
+    """With one split the split pass normalises and writes O and LSE itself (no merge
+    launch), for every head-group size; an empty sequence gives O = 0, LSE = -inf."""
+    out, lse = _run(3, 32, Hkv, [300, 0, 1], D, dtype, Scap=300, seed=31, num_splits=1)
+    assert np.all(to_f64(out)[1] == 0) and np.all(to_f64(lse)[1] == -np.inf)
+
+
 def test_finite_bias_mask_added_after_scale():
     _run(2, 32, 32, [1500, 700], 128, "f16", bias_seed=5, seed=2)
 
