@@ -71,6 +71,10 @@ void fwd_fp8_kernel(FwdParams p) {
     constexpr float kRescale = 8.f;
     static_assert(NL >= 1 && NL * NW == 2 * KBLK && KBLK % NL == 0, "tile shape");
 
+    // no score_mod and no mask: the fixed-max fast path (see the end of the kernel)
+    constexpr bool FAST = MASK == 0 && !ALIBI;
+    __shared__ int wg_failed;
+
     // three stages, each a K tile then a V tile
     __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
     __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
@@ -352,59 +356,74 @@ void fwd_fp8_kernel(FwdParams p) {
         cls = 1;
         return t + 1 < kt_hi ? t + 1 : END;
     };
-    int c_cur, c_nxt, c_aft;
-    int cur;
-    if (MASK & MASK_BLOCK) {
-        cur = walk.next(0, lane, c_cur);
-        if (cur >= kt_hi) cur = END;
-    } else {
-        cur = kt_lo < kt_hi ? kt_lo : END;
-        c_cur = 1;
-    }
-    if (cur < END) {
+    // One pass over the row's tiles. fast: the row's max is fixed by its first tile and
+    // later tiles neither take their max nor rescale (no score_mod, unmasked only; see
+    // below); otherwise the lazy rescale. compute: this wave computes; a wave that does
+    // not only copies its share of each tile and meets the barriers.
+    auto run = [&](bool fast, bool compute) __attribute__((always_inline)) {
+        int c_cur, c_nxt, c_aft;
+        int cur;
+        if (MASK & MASK_BLOCK) {
+            cur = walk.next(0, lane, c_cur);
+            if (cur >= kt_hi) cur = END;
+        } else {
+            cur = kt_lo < kt_hi ? kt_lo : END;
+            c_cur = 1;
+        }
+        if (cur >= END) return;
         int nxt = next_tile(cur, c_nxt);
         int aft = next_tile(nxt, c_aft);
         load_tile(cur, kv0);
         load_tile(nxt < END ? nxt : cur, kv1);
         kv_barrier<0>();
         f32x16 s_cur[NKB];
-        qk(kv0, s_cur);
-        float cc_cur = transform(cur, c_cur, s_cur);
-        rescale(tile_max(s_cur, cc_cur));
-        auto body = [&](unsigned char *Sc, unsigned char *Sn, unsigned char *Sa) {
+        float cc_cur = 1.f;
+        if (compute) {
+            qk(kv0, s_cur);
+            cc_cur = transform(cur, c_cur, s_cur);
+            rescale(tile_max(s_cur, cc_cur));
+        }
+        auto body = [&](unsigned char *Sc, unsigned char *Sn, unsigned char *Sa) __attribute__((always_inline)) {
             load_tile(aft < END ? aft : cur, Sa);
             f32x16 s_nxt[NKB];
-            qk(Sn, s_nxt);
-            int pp[8];
-            expcvt(s_cur, cc_cur, pp);
-            lacc = mfma_fp8(ones, i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]}, lacc);
-            // interleave: the K reads first, then each MFMA of S(t_{n+1}) followed by a
-            // share of the exponentials of t_n
-            __builtin_amdgcn_sched_group_barrier(0x100, NKB * NC * 2, 0);
+            float cc_nxt = 1.f;
+            if (compute) {
+                qk(Sn, s_nxt);
+                int pp[8];
+                expcvt(s_cur, cc_cur, pp);
+                lacc = mfma_fp8(ones, i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]}, lacc);
+                // interleave: the K reads first, then each MFMA of S(t_{n+1}) followed by
+                // a share of the exponentials of t_n
+                __builtin_amdgcn_sched_group_barrier(0x100, NKB * NC * 2, 0);
 #pragma unroll
-            for (int i = 0; i < NKB * NC; ++i) {
+                for (int i = 0; i < NKB * NC; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+                }
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            const float cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, s_nxt);
-            pv(Sc + TILEB, pp);
-            const float mloc = tile_max(s_nxt, cc_nxt);
-            // then the V reads, and each MFMA of P V followed by a share of the max
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);
+                cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, s_nxt);
+                pv(Sc + TILEB, pp);
+                if (!fast) {
+                    const float mloc = tile_max(s_nxt, cc_nxt);
+                    // then the V reads, and each MFMA of P V followed by a share of the max
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);
 #pragma unroll
-            for (int i = 0; i < DB + 1; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    for (int i = 0; i < DB + 1; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    }
+                    // a tile past the end must not move the running max
+                    rescale(nxt < END ? mloc : -INFINITY);
+                }
             }
-            // a tile past the end must not move the running max
-            rescale(nxt < END ? mloc : -INFINITY);
             kv_barrier<0>();
+            if (compute) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
-            cc_cur = cc_nxt;
+                for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
+                cc_cur = cc_nxt;
+            }
         };
-        auto advance = [&]() {
+        auto advance = [&]() __attribute__((always_inline)) {
             cur = nxt;
             c_cur = c_nxt;
             nxt = aft;
@@ -422,6 +441,106 @@ void fwd_fp8_kernel(FwdParams p) {
             if (nxt >= END) break;
             advance();
         }
+    };
+
+    if constexpr (FAST) {
+        // Without a score_mod or mask the row's max is fixed by its first tile, and later
+        // tiles exponentiate against it without taking their own max (32 maxima, a
+        // cross-lane exchange and the rescale test per wave-tile). A P above e4m3's range
+        // (a score more than about 8.9, base 2, above that max) converts to NaN, which the
+        // all-ones product carries into the row sum; a row whose sum is not finite marks
+        // its wave, and the workgroup then streams the tiles once more: the failed waves
+        // recompute from scratch with the lazy rescale (every P at most 2^8), the others
+        // only copy.
+        if (tid == 0) wg_failed = 0;
+        run(true, true);
+        const bool wave_failed = __builtin_amdgcn_ballot_w64(!(lacc[0] <= 3.0e38f)) != 0;
+        if (wave_failed && lane == 0) wg_failed = 1;
+        __syncthreads();
+        if (wg_failed) {
+            if (wave_failed) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+                lacc = f32x16{};
+                m_run = -INFINITY;
+            }
+            run(false, wave_failed);
+        }
+    } else {
+        // every other case: one pass with the lazy rescale (the loop above written out
+        // once more, so that these kernels compile exactly as before the fast path)
+        int c_cur, c_nxt, c_aft;
+        int cur;
+        if (MASK & MASK_BLOCK) {
+            cur = walk.next(0, lane, c_cur);
+            if (cur >= kt_hi) cur = END;
+        } else {
+            cur = kt_lo < kt_hi ? kt_lo : END;
+            c_cur = 1;
+        }
+        if (cur < END) {
+            int nxt = next_tile(cur, c_nxt);
+            int aft = next_tile(nxt, c_aft);
+            load_tile(cur, kv0);
+            load_tile(nxt < END ? nxt : cur, kv1);
+            kv_barrier<0>();
+            f32x16 s_cur[NKB];
+            qk(kv0, s_cur);
+            float cc_cur = transform(cur, c_cur, s_cur);
+            rescale(tile_max(s_cur, cc_cur));
+            auto body = [&](unsigned char *Sc, unsigned char *Sn, unsigned char *Sa) {
+                load_tile(aft < END ? aft : cur, Sa);
+                f32x16 s_nxt[NKB];
+                qk(Sn, s_nxt);
+                int pp[8];
+                expcvt(s_cur, cc_cur, pp);
+                lacc = mfma_fp8(ones, i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]}, lacc);
+                // interleave: the K reads first, then each MFMA of S(t_{n+1}) followed by a
+                // share of the exponentials of t_n
+                __builtin_amdgcn_sched_group_barrier(0x100, NKB * NC * 2, 0);
+    #pragma unroll
+                for (int i = 0; i < NKB * NC; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                const float cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, s_nxt);
+                pv(Sc + TILEB, pp);
+                const float mloc = tile_max(s_nxt, cc_nxt);
+                // then the V reads, and each MFMA of P V followed by a share of the max
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);
+    #pragma unroll
+                for (int i = 0; i < DB + 1; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+                // a tile past the end must not move the running max
+                rescale(nxt < END ? mloc : -INFINITY);
+                kv_barrier<0>();
+    #pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
+                cc_cur = cc_nxt;
+            };
+            auto advance = [&]() {
+                cur = nxt;
+                c_cur = c_nxt;
+                nxt = aft;
+                c_nxt = c_aft;
+                aft = next_tile(aft, c_aft);
+            };
+            for (;;) {
+                body(kv0, kv1, kv2);
+                if (nxt >= END) break;
+                advance();
+                body(kv1, kv2, kv0);
+                if (nxt >= END) break;
+                advance();
+                body(kv2, kv0, kv1);
+                if (nxt >= END) break;
+                advance();
+            }
+        }
+
     }
 
     // ---- epilogue: both lane halves hold the whole row sum in lacc ----

@@ -205,3 +205,26 @@ def test_random_document_mask_within_derived_bound(D):
     docs = inputs.packed_document_ids(11, 2, 1024, 7)
     _run(x, D, scale=float(np.float32(1 / math.sqrt(D))), exact=False, causal=True, alibi=True,
          q_doc=docs, label="doc")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_scores_far_above_the_first_tile(D):
+    """Without a mod the kernel fixes each row's max at its first key tile. Here half the
+    rows (alternating blocks of 8) see their lowest scores in that tile and scores up to
+    8 units (23 in base 2 at this scale) higher later, so their P overflow e4m3 and the
+    workgroup recomputes those waves with the lazy rescale; the other rows see their
+    highest scores first and keep the first pass. Random V; the derived bound applies."""
+    B, H, Sq, Skv = 1, 2, 512, 1024
+    g = inputs.rng(41)
+    sign = np.where((np.arange(Sq) // 8) % 2 == 0, 1.0, -1.0)
+    q = np.zeros((B, H, Sq, D))
+    q[..., :4] = sign[None, None, :, None]
+    k = g.choice([-1.0, 0.0, 1.0], size=(B, H, Skv, D))
+    k[..., :64, :4] = -1.0          # first tile: score -4 for rows of sign +1 (+4 for sign -1)
+    k[..., 64:, 4:] = 0.0
+    v = g.standard_normal((B, H, Skv, D)).astype(np.float32)
+    dv = np.float32(float(np.abs(v).max()) / inputs.E4M3_MAX)
+    x = {"q": inputs.f32_to_e4m3_bits(q), "k": inputs.f32_to_e4m3_bits(k),
+         "v": inputs.f32_to_e4m3_bits(np.clip(v / dv, -448, 448)),
+         "descale_q": 1.0, "descale_k": 1.0, "descale_v": float(dv)}
+    _run(x, D, scale=2.0, exact=False, label="far-above")
