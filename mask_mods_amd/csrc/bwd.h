@@ -64,8 +64,12 @@ void bwd_dq_kernel(BwdParams p) {
     typedef typename TT::vec8 V8;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
+    // with the document mask a stage also holds its tile's 64 key document ids, so that
+    // the tile reads them from LDS (a global load inside the tile would make the compiler
+    // wait for every copy in flight, the next tile's included)
+    constexpr int DOCB = (MASK & MASK_DOC) ? 1024 : 0;
+    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB + DOCB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB + DOCB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -159,6 +163,10 @@ void bwd_dq_kernel(BwdParams p) {
         const int k0 = kt * BN;
         const uint32_t kl = lds_addr(kdst) + (uint32_t)(wave_s * LOADS) * 1024u;
         const uint32_t vl = lds_addr(vdst) + (uint32_t)(wave_s * LOADS) * 1024u;
+        if ((MASK & MASK_DOC) && wave_s == 0) {
+            // the tile's key document ids (clamped to the last key) after its V tile
+            dma4_vaddr(p.kvdoc + b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1), lds_addr(kdst) + 2 * TILEB);
+        }
         if (k0 + BN <= p.Skv) {
             const char *kb = (const char *)(kg + (int64_t)k0 * p.k_ss);
             const char *vb = (const char *)(vg + (int64_t)k0 * p.v_ss);
@@ -197,9 +205,9 @@ void bwd_dq_kernel(BwdParams p) {
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
         bool doc_mask = false;
+        const int32_t *kd = (const int32_t *)(Kt + 2 * TILEB);  // the tile's key ids, clamped
         if ((MASK & MASK_DOC) && pred && !skip) {
-            const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
-            const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
+            const int kdl = kd[0], kdh = kd[BN - 1];
             skip |= kdh < wd_lo || kdl > wd_hi;
             doc_mask = !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
             need_mask |= doc_mask;
@@ -207,8 +215,7 @@ void bwd_dq_kernel(BwdParams p) {
         if (skip) return;
         // a tile that straddles documents: the lane's document's keys, [dfirst, dend)
         int dfirst = 0, dend = BN;
-        if ((MASK & MASK_DOC) && doc_mask)
-            tile_doc_range(p.kvdoc[b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1)], mydoc, dfirst, dend);
+        if ((MASK & MASK_DOC) && doc_mask) tile_doc_range(kd[lane], mydoc, dfirst, dend);
         // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T, then dS^T, then
         // dQ^T += K^T dS^T over the block's two 16-key k-steps
         const bool general = ALIBI || need_mask;
@@ -348,8 +355,10 @@ void bwd_dkdv_kernel(BwdParams p) {
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
     static_assert(kBwdRowPad % BQ == 0, "workspace row padding");
 
-    // per stage: Q tile, dO tile, then the tile rows' lse2 and D (64 floats each)
-    constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;
+    // per stage: Q tile, dO tile, then the tile rows' lse2 and D (64 floats each), and
+    // with the document mask their 64 query document ids (read from LDS by the tile: a
+    // global load inside it would make the compiler wait for the copy in flight)
+    constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4 + ((MASK & MASK_DOC) ? BQ * 4 : 0);
     __shared__ __attribute__((aligned(1024))) unsigned char qd0[STAGEB];
     __shared__ __attribute__((aligned(1024))) unsigned char qd1[STAGEB];
 
@@ -447,6 +456,8 @@ void bwd_dkdv_kernel(BwdParams p) {
             const uint32_t sl = lds_addr(dst) + 2 * TILEB;
             dma4_vaddr(p.ws_lse2 + w, sl);
             dma4_vaddr(p.ws_dd + w, sl + BQ * 4);
+            // the rows' document ids, clamped to the last row
+            if (MASK & MASK_DOC) dma4_vaddr(p.qdoc + b * p.qdoc_sb + min(i0 + lane, p.Sq - 1), sl + 2 * BQ * 4);
         }
         if (i0 + BQ <= p.Sq) {
             const char *qb = (const char *)(qg + (int64_t)i0 * p.q_ss);
@@ -493,9 +504,9 @@ void bwd_dkdv_kernel(BwdParams p) {
             need_mask |= max(i_last - kw0, kw0 + 31 - i0) > p.window;
         }
         bool doc_mask = false;
+        const int32_t *qd = (const int32_t *)(Qt + 2 * TILEB + 2 * BQ * 4);  // the rows' ids, clamped
         if ((MASK & MASK_DOC) && pred && !skip) {
-            const int32_t *qd = p.qdoc + b * p.qdoc_sb;
-            const int qdl = qd[i0], qdh = qd[min(i_last, p.Sq - 1)];
+            const int qdl = qd[0], qdh = qd[BQ - 1];
             skip |= qdh < wk_lo || qdl > wk_hi;
             doc_mask = !(wk_lo == wk_hi && qdl == qdh && qdl == wk_lo);
             need_mask |= doc_mask;
@@ -504,8 +515,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         // a tile that straddles documents: the rows of the lane's key's document,
         // [dfirst, dend) as offsets in the 64-row tile
         int dfirst = 0, dend = BQ;
-        if ((MASK & MASK_DOC) && doc_mask)
-            tile_doc_range(p.qdoc[b * p.qdoc_sb + min(i0 + lane, p.Sq - 1)], mykdoc, dfirst, dend);
+        if ((MASK & MASK_DOC) && doc_mask) tile_doc_range(qd[lane], mykdoc, dfirst, dend);
         // per-lane rows of block rb of the accumulator: i0 + 32*rb + 8*a + 4*hi + (0..3),
         // their lse2 and D from the copy in LDS (pad rows hold no data and are masked)
         const float *sl2 = (const float *)(Qt + 2 * TILEB), *sdd = sl2 + BQ;

@@ -75,10 +75,13 @@ void fwd_fp8_kernel(FwdParams p) {
     constexpr bool FAST = MASK == 0 && !ALIBI;
     __shared__ int wg_failed;
 
-    // three stages, each a K tile then a V tile
-    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kv2[2 * TILEB];
+    // three stages, each a K tile then a V tile, then with the document mask the tile's 64
+    // key document ids (read from LDS: a global load in a tile would make the compiler wait
+    // for every copy in flight, the next tile's included)
+    constexpr int DOCB = (MASK & MASK_DOC) ? 1024 : 0;
+    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB + DOCB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB + DOCB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv2[2 * TILEB + DOCB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -182,6 +185,8 @@ void fwd_fp8_kernel(FwdParams p) {
     auto load_tile = [&](int kt, unsigned char *kdst) {
         const int k0 = kt * BN;
         const uint32_t dst = lds_addr(kdst) + (cp_v ? (uint32_t)TILEB : 0u) + (uint32_t)blk0 * 1024u;
+        if ((MASK & MASK_DOC) && wave_s == 0)
+            dma4_vaddr(p.kvdoc + b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1), lds_addr(kdst) + 2 * TILEB);
         if (k0 + BN <= p.Skv) {
             const uint8_t *base = cp_src + (int64_t)k0 * cp_ss;
 #pragma unroll
@@ -228,7 +233,7 @@ void fwd_fp8_kernel(FwdParams p) {
     // scale / score_mod / mask_mod where the tile needs them; returns the multiplier the
     // exponent (and the max) apply to sacc: 1 when sacc was rewritten as base-2 scores,
     // else the scale (plain tiles keep the raw dot products)
-    auto transform = [&](int kt, int blk, f32x16 (&sacc)[NKB]) -> float {
+    auto transform = [&](int kt, int blk, const unsigned char *St, f32x16 (&sacc)[NKB]) -> float {
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
         const bool pred = blk == 1;
@@ -242,9 +247,9 @@ void fwd_fp8_kernel(FwdParams p) {
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
         bool doc_mask = false;
+        const int32_t *kd = (const int32_t *)(St + 2 * TILEB);  // the tile's key ids, clamped
         if ((MASK & MASK_DOC) && pred) {
-            const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
-            const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
+            const int kdl = kd[0], kdh = kd[BN - 1];
             dead |= kdh < wd_lo || kdl > wd_hi;
             doc_mask = !dead && !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
             need_mask |= !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
@@ -253,8 +258,7 @@ void fwd_fp8_kernel(FwdParams p) {
         const float base = ALIBI ? slope2 * (float)(k0 + 4 * hi - row) : 0.f;
         // a tile that straddles documents: the lane's document's keys, [dfirst, dend)
         int dfirst = 0, dend = BN;
-        if ((MASK & MASK_DOC) && doc_mask)
-            tile_doc_range(p.kvdoc[b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1)], mydoc, dfirst, dend);
+        if ((MASK & MASK_DOC) && doc_mask) tile_doc_range(kd[lane], mydoc, dfirst, dend);
         // the lane's kept keys in the tile: one interval of offsets jo = j - k0 - 4*hi
         // (each predicate keeps an interval; a dead tile keeps none)
         const int rel = row - k0 - 4 * hi;
@@ -380,7 +384,7 @@ void fwd_fp8_kernel(FwdParams p) {
         float cc_cur = 1.f;
         if (compute) {
             qk(kv0, s_cur);
-            cc_cur = transform(cur, c_cur, s_cur);
+            cc_cur = transform(cur, c_cur, kv0, s_cur);
             rescale(tile_max(s_cur, cc_cur));
         }
         auto body = [&](unsigned char *Sc, unsigned char *Sn, unsigned char *Sa) __attribute__((always_inline)) {
@@ -401,7 +405,7 @@ void fwd_fp8_kernel(FwdParams p) {
                     __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, s_nxt);
+                cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, Sn, s_nxt);
                 pv(Sc + TILEB, pp);
                 if (!fast) {
                     const float mloc = tile_max(s_nxt, cc_nxt);
@@ -486,7 +490,7 @@ void fwd_fp8_kernel(FwdParams p) {
             kv_barrier<0>();
             f32x16 s_cur[NKB];
             qk(kv0, s_cur);
-            float cc_cur = transform(cur, c_cur, s_cur);
+            float cc_cur = transform(cur, c_cur, kv0, s_cur);
             rescale(tile_max(s_cur, cc_cur));
             auto body = [&](unsigned char *Sc, unsigned char *Sn, unsigned char *Sa) {
                 load_tile(aft < END ? aft : cur, Sa);
@@ -504,7 +508,7 @@ void fwd_fp8_kernel(FwdParams p) {
                     __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                const float cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, s_nxt);
+                const float cc_nxt = transform(nxt < END ? nxt : cur, c_nxt, Sn, s_nxt);
                 pv(Sc + TILEB, pp);
                 const float mloc = tile_max(s_nxt, cc_nxt);
                 // then the V reads, and each MFMA of P V followed by a share of the max

@@ -59,8 +59,12 @@ void fwd_mfma_kernel(FwdParams p) {
     // every tile reads a statically known buffer while the DMA fills the other, and the
     // compiler can see the reads never alias the in-flight copies (no early vmcnt wait).
     // (one object per stage, K then V: the waitcnt pass tracks only a few DMA targets)
-    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB];
+    // with the document mask a stage also holds its tile's 64 key document ids (copied
+    // with K and V), so that a tile reads them from LDS: a global load inside the tile
+    // would make the compiler wait for every copy in flight, the next tile's included
+    constexpr int DOCB = (MASK & MASK_DOC) ? 1024 : 0;
+    __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB + DOCB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB + DOCB];
     unsigned char *const KB[2] = {kv0, kv1};
     unsigned char *const VB[2] = {kv0 + TILEB, kv1 + TILEB};
 
@@ -174,6 +178,10 @@ void fwd_mfma_kernel(FwdParams p) {
         const int k0 = kt * BN;
         const uint32_t kl = lds_addr(kdst) + (uint32_t)(wave_s * LOADS) * 1024u;
         const uint32_t vl = lds_addr(vdst) + (uint32_t)(wave_s * LOADS) * 1024u;
+        if ((MASK & MASK_DOC) && wave_s == 0) {
+            // the tile's key document ids (clamped to the last key) after its V tile
+            dma4_vaddr(p.kvdoc + b * p.kvdoc_sb + min(k0 + lane, p.Skv - 1), lds_addr(kdst) + 2 * TILEB);
+        }
         if (k0 + BN <= p.Skv) {
             const char *kb = (const char *)(kg + (int64_t)k0 * p.k_ss);
             const char *vb = (const char *)(vg + (int64_t)k0 * p.v_ss);
@@ -201,7 +209,7 @@ void fwd_mfma_kernel(FwdParams p) {
     // Whether this wave skips tile kt, and whether the tile needs per-pair masking.
     // `blk` is the tile's block-mask class: 1 = the mask_mod predicates decide,
     // 2 = every pair kept (predicates not evaluated).
-    auto classify = [&](int kt, int blk, bool &need_mask, bool &doc_mask) -> bool {
+    auto classify = [&](int kt, int blk, const unsigned char *Kt, bool &need_mask, bool &doc_mask) -> bool {
         const int k0 = kt * BN;
         const int r_last = r0 + 31;
         const bool pred = blk == 1;  // predicates apply in this tile
@@ -217,8 +225,8 @@ void fwd_mfma_kernel(FwdParams p) {
             need_mask |= max(r_last - k0, k0 + BN - 1 - r0) > p.window;
         }
         if ((MASK & MASK_DOC) && pred && !skip) {
-            const int32_t *kd = p.kvdoc + b * p.kvdoc_sb;
-            const int kdl = kd[k0], kdh = kd[min(k0 + BN - 1, p.Skv - 1)];
+            const int32_t *kd = (const int32_t *)(Kt + 2 * TILEB);  // the tile's ids, clamped
+            const int kdl = kd[0], kdh = kd[BN - 1];
             skip |= kdh < wd_lo || kdl > wd_hi;
             doc_mask = !(wd_lo == wd_hi && kdl == kdh && kdl == wd_lo);
             need_mask |= doc_mask;
@@ -432,11 +440,10 @@ void fwd_mfma_kernel(FwdParams p) {
                     unsigned char *Kn, unsigned char *Vn) {
         if (next >= 0) load_tile(next, Kn, Vn);
         bool need_mask, doc_mask;
-        if (!classify(kt, blk, need_mask, doc_mask)) {
-            // a tile that straddles documents: its 64 key ids, loaded before the QK
-            // products so that the load is in flight while they run
+        if (!classify(kt, blk, Kt, need_mask, doc_mask)) {
+            // a tile that straddles documents: its 64 key ids, one per lane, from LDS
             int tdoc = 0;
-            if ((MASK & MASK_DOC) && doc_mask) tdoc = p.kvdoc[b * p.kvdoc_sb + min(kt * BN + lane, p.Skv - 1)];
+            if ((MASK & MASK_DOC) && doc_mask) tdoc = ((const int32_t *)(Kt + 2 * TILEB))[lane];
             f32x16 sacc[NKB];
             qk(Kt, sacc);
             uint32_t pp[NKB][8];
