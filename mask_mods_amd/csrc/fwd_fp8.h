@@ -86,9 +86,9 @@ void fwd_fp8_kernel(FwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
 
-    // causal: the last query tiles carry the most keys; they start first
+    // causal without a window: the last query tiles carry the most keys; they start first
     int qt, pair;
-    work_item(blockIdx.x, gridDim.x, p.n_qtiles, (MASK & MASK_CAUSAL) != 0, qt, pair);
+    work_item(blockIdx.x, gridDim.x, p.n_qtiles, longest_first(MASK), qt, pair);
     const int h = pair % p.Hq;
     const int b = pair / p.Hq;
     const int q0 = qt * BM;

@@ -71,9 +71,9 @@ void fwd_mfma_kernel(FwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
 
-    // causal: the last query tiles carry the most keys; they start first
+    // causal without a window: the last query tiles carry the most keys; they start first
     int qt, pair;
-    work_item(blockIdx.x, gridDim.x, p.n_qtiles, (MASK & MASK_CAUSAL) != 0, qt, pair);
+    work_item(blockIdx.x, gridDim.x, p.n_qtiles, longest_first(MASK), qt, pair);
     const int h = pair % p.Hq;
     const int b = pair / p.Hq;
     const int q0 = qt * BM;
@@ -90,8 +90,11 @@ void fwd_mfma_kernel(FwdParams p) {
     const int row = r0 + l32;       // the row this lane owns
 
     // Q^T fragments (B operand): row `row`, dims 16*ks + 8*hi .. +7
+    // 4-wave workgroups copy their 128 Q rows to LDS instead (below): whole rows per
+    // copy instruction rather than 32 bytes of 32 rows per lane load
+    constexpr bool QLDS = NW == 4;
     V8 qf[KS];
-    {
+    if (!QLDS) {
         const bool ok = row < p.Sq;
         const uint16_t *qr = qg + (int64_t)(ok ? row : 0) * p.q_ss + 8 * hi;
 #pragma unroll
@@ -198,6 +201,25 @@ void fwd_mfma_kernel(FwdParams p) {
                 dma16_vaddr(vg + (int64_t)gr * p.v_ss + 8 * tchunk[i], vl + i * 1024);
             }
         }
+    };
+
+    // Q rows q0 .. q0+127 (clamped to the last row) as two 64-row tiles in stage 1, in the
+    // K tile layout, copied with the first K/V tile; each wave then reads its rows'
+    // fragments as the K fragments are read, and a barrier frees stage 1 for the loop
+    auto q_copy = [&]() {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int gr = min(q0 + 64 * t2 + trow[i], p.Sq - 1);
+                dma16_vaddr(qg + (int64_t)gr * p.q_ss + 8 * tchunk[i],
+                            lds_addr(kv1) + (uint32_t)(t2 * TILEB + (wave_s * LOADS + i) * 1024));
+            }
+    };
+    auto q_read = [&]() {
+        const unsigned char *qs = kv1 + wave_s * 32 * TL::ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const V8 *)(qs + koff[ks]);
     };
 
     f32x16 oacc[DB];
@@ -459,8 +481,13 @@ void fwd_mfma_kernel(FwdParams p) {
         int cv, nv;
         int cur = next_block(0, cv);
         int nxt = cur < nkb ? next_block(cur + 1, nv) : nkb;
+        if (QLDS) q_copy();
         if (cur < nkb) load_tile(cur, KB[0], VB[0]);
         kv_barrier<0>();
+        if (QLDS) {
+            q_read();
+            kv_barrier<0>();
+        }
         while (cur < nkb) {
             tile(cur, cv, KB[0], VB[0], nxt < nkb ? nxt : -1, KB[1], VB[1]);
             kv_barrier<0>();
@@ -475,8 +502,13 @@ void fwd_mfma_kernel(FwdParams p) {
             if (cur < nkb) nxt = next_block(cur + 1, nv);
         }
     } else {
+        if (QLDS) q_copy();
         if (kt_lo < kt_hi) load_tile(kt_lo, KB[0], VB[0]);
         kv_barrier<0>();
+        if (QLDS) {
+            q_read();
+            kv_barrier<0>();
+        }
         for (int kt = kt_lo; kt < kt_hi; kt += 2) {
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -498,21 +530,31 @@ void fwd_mfma_kernel(FwdParams p) {
     }
     const bool live = l_tot > 0.f && !dropped;
     const float inv = live ? 1.f / l_tot : 0.f;
-    if (row < p.Sq) {
-        uint16_t *og = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss;
+    // O through LDS (every wave is past its last tile): the wave writes its 32 rows into
+    // its own 32-row slice in the K tile layout, then stores whole rows, 16 bytes per lane
+    // (a lane's own fragments are 8 bytes in each of 32 rows per store instruction)
+    unsigned char *os = (wave_s < 4 ? kv0 : kv1) + (wave_s & 3) * 32 * TL::ROWB;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 x = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
-                                 oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-                *(typename TT::vec4 *)(og + 32 * db + 8 * g4 + 4 * hi) = cvt4(x, TT{});
-            }
-        }
-        if (hi == 0 && p.lse) {
-            p.lse[((int64_t)b * p.Hq + h) * p.Sq + row] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 x = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
+                             oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+            *(typename TT::vec4 *)(os + TL::off(l32, 4 * db + g4) + 8 * hi) = cvt4(x, TT{});
         }
     }
+    {
+        constexpr int RPS = 64 / TL::CH;  // rows per store instruction
+        uint16_t *ob = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh;
+#pragma unroll
+        for (int i = 0; i < 32 / RPS; ++i) {
+            const int rr = i * RPS + lane / TL::CH, c = lane % TL::CH;
+            const u32x4 y = *(const u32x4 *)(os + TL::off(rr, c));
+            if (r0 + rr < p.Sq) *(u32x4 *)(ob + (int64_t)(r0 + rr) * p.o_ss + 8 * c) = y;
+        }
+    }
+    if (row < p.Sq && hi == 0 && p.lse)
+        p.lse[((int64_t)b * p.Hq + h) * p.Sq + row] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 

@@ -395,7 +395,10 @@ void fwd_pipe_kernel(FwdParams p) {
             if (n < n_end) kv_barrier<0>();
         }
     };
-    auto epilogue = [&]() __attribute__((always_inline)) {
+    // staged: every wave of the workgroup is past its last tile, so the LDS is free: the
+    // wave writes its 32 rows of O into its own slice (K tile layout) and stores whole
+    // rows, 16 bytes per lane, instead of 8 bytes in each of 32 rows per instruction
+    auto epilogue = [&](bool staged) __attribute__((always_inline)) {
         const float l_tot = l_run + __shfl_xor(l_run, 32);
         bool dropped = false;
         if (p.rowdrop) {
@@ -404,7 +407,28 @@ void fwd_pipe_kernel(FwdParams p) {
         }
         const bool live = l_tot > 0.f && !dropped;
         const float inv = live ? 1.f / l_tot : 0.f;
-        if (row < p.Sq) {
+        if (staged) {
+            unsigned char *os = smem + wave_s * 32 * TL::ROWB;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 x = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
+                                     oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+                    *(typename TT::vec4 *)(os + TL::off(l32, 4 * db + g4) + 8 * hi) = cvt4(x, TT{});
+                }
+            }
+            constexpr int RPS = 64 / TL::CH;  // rows per store instruction
+            uint16_t *ob = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh;
+#pragma unroll
+            for (int i = 0; i < 32 / RPS; ++i) {
+                const int rr = i * RPS + lane / TL::CH, c = lane % TL::CH;
+                const u32x4 y = *(const u32x4 *)(os + TL::off(rr, c));
+                if (r0 + rr < p.Sq) *(u32x4 *)(ob + (int64_t)(r0 + rr) * p.o_ss + 8 * c) = y;
+            }
+            if (row < p.Sq && hi == 0 && p.lse)
+                p.lse[((int64_t)b * p.Hq + h) * p.Sq + row] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        } else if (row < p.Sq) {
             uint16_t *og = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -451,13 +475,13 @@ void fwd_pipe_kernel(FwdParams p) {
     if (failed && lane == 0) wg_failed = 1;
     kv_barrier<0>();
     const bool again = wg_failed != 0;
-    if (!failed) epilogue();
+    if (!failed) epilogue(!again);
     if (again) {
         if (failed) {
             run_max();
             kv_barrier<0>();
             run();
-            epilogue();
+            epilogue(false);
         } else {
             run_idle();
             kv_barrier<0>();

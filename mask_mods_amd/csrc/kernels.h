@@ -9,6 +9,13 @@ namespace mm {
 
 enum { MASK_CAUSAL = 1, MASK_WINDOW = 2, MASK_BLOCK = 4, MASK_DOC = 8 };
 
+// Whether a causal forward starts its heaviest tiles first: not with a window, whose
+// tiles carry equal work and are better run side by side, neighbours of one (b, h) on
+// one XCD, so that the K/V they share is served by its L2 (3-4% at window 256). Packed
+// documents keep the causal order (10% faster than side by side at 16 documents, forward
+// and backward); the backward keeps it with a window too.
+constexpr bool longest_first(int mask) { return (mask & MASK_CAUSAL) && !(mask & MASK_WINDOW); }
+
 // block-mask granularity: query rows x keys per block
 constexpr int kBlockQ = 128, kBlockKV = 64;
 
