@@ -59,20 +59,30 @@ __device__ __forceinline__ void kv_barrier() {
 // Wave-wide search on a non-decreasing int32 array of n entries for both ends of a
 // range: the first index whose value is >= vlo and the first whose value is > vhi (n if
 // none). n, vlo and vhi are wave-uniform and every lane of the wave takes part. Each
-// round probes up to 64 evenly spaced entries per search (one load per lane); the
-// probes that lie before the answer form a prefix, counted with a ballot, and the answer
-// lies between the last of them and the next probe. 8192 entries take three rounds,
-// the two searches sharing them so that their loads are in flight together.
+// round probes up to 128 evenly spaced entries per search (two loads per lane, probe
+// lane + 64 j at lo + (lane + 64 j) * step); the probes that lie before the answer form
+// a prefix, counted with two ballots, and the answer lies between the last of them and
+// the next probe. Up to 16384 entries take two rounds of dependent loads, the two
+// searches sharing them so that all four loads of a lane are in flight together.
 __device__ __forceinline__ void wave_search_range(const int32_t *a, int n, int vlo, int vhi, int lane,
                                                   int &out_lo, int &out_hi) {
     int lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
     while (lo1 < hi1 || lo2 < hi2) {
-        const int st1 = (hi1 - lo1 + 63) >> 6, st2 = (hi2 - lo2 + 63) >> 6;
-        const int i1 = lo1 + lane * st1, i2 = lo2 + lane * st2;
-        const int x1 = lo1 < hi1 ? a[min(i1, hi1 - 1)] : 0;
-        const int x2 = lo2 < hi2 ? a[min(i2, hi2 - 1)] : 0;
-        const int c1 = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i1 < hi1 && x1 < vlo));
-        const int c2 = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i2 < hi2 && x2 <= vhi));
+        const int st1 = (hi1 - lo1 + 127) >> 7, st2 = (hi2 - lo2 + 127) >> 7;
+        int i1[2], i2[2], x1[2], x2[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            i1[j] = lo1 + (lane + 64 * j) * st1;
+            i2[j] = lo2 + (lane + 64 * j) * st2;
+            x1[j] = lo1 < hi1 ? a[min(i1[j], hi1 - 1)] : 0;
+            x2[j] = lo2 < hi2 ? a[min(i2[j], hi2 - 1)] : 0;
+        }
+        int c1 = 0, c2 = 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            c1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i1[j] < hi1 && x1[j] < vlo));
+            c2 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i2[j] < hi2 && x2[j] <= vhi));
+        }
         if (lo1 < hi1) {
             if (c1 == 0) hi1 = lo1;
             else {

@@ -90,11 +90,25 @@ void fwd_mfma_kernel(FwdParams p) {
     const int row = r0 + l32;       // the row this lane owns
 
     // Q^T fragments (B operand): row `row`, dims 16*ks + 8*hi .. +7
-    // 4-wave workgroups copy their 128 Q rows to LDS instead (below): whole rows per
-    // copy instruction rather than 32 bytes of 32 rows per lane load
+    // 4-wave workgroups copy their 128 Q rows to LDS instead: whole rows per copy
+    // instruction rather than 32 bytes of 32 rows per lane load. Rows q0 .. q0+127
+    // (clamped to the last row) become two 64-row tiles in stage 1, in the K tile layout;
+    // the copy is issued first, so that it is in flight during the key-range search and
+    // the first K/V copy. Each wave reads its rows' fragments as the K fragments are
+    // read (q_read below), and a barrier then frees stage 1 for the loop.
     constexpr bool QLDS = NW == 4;
     V8 qf[KS];
-    if (!QLDS) {
+    if (QLDS) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int r = (wave_s * LOADS + i) * RPI + lane / TL::CH;
+                const int gr = min(q0 + 64 * t2 + r, p.Sq - 1);
+                dma16_vaddr(qg + (int64_t)gr * p.q_ss + 8 * ((lane % TL::CH) ^ TL::swz(r)),
+                            lds_addr(kv1) + (uint32_t)(t2 * TILEB + (wave_s * LOADS + i) * 1024));
+            }
+    } else {
         const bool ok = row < p.Sq;
         const uint16_t *qr = qg + (int64_t)(ok ? row : 0) * p.q_ss + 8 * hi;
 #pragma unroll
@@ -203,19 +217,6 @@ void fwd_mfma_kernel(FwdParams p) {
         }
     };
 
-    // Q rows q0 .. q0+127 (clamped to the last row) as two 64-row tiles in stage 1, in the
-    // K tile layout, copied with the first K/V tile; each wave then reads its rows'
-    // fragments as the K fragments are read, and a barrier frees stage 1 for the loop
-    auto q_copy = [&]() {
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int gr = min(q0 + 64 * t2 + trow[i], p.Sq - 1);
-                dma16_vaddr(qg + (int64_t)gr * p.q_ss + 8 * tchunk[i],
-                            lds_addr(kv1) + (uint32_t)(t2 * TILEB + (wave_s * LOADS + i) * 1024));
-            }
-    };
     auto q_read = [&]() {
         const unsigned char *qs = kv1 + wave_s * 32 * TL::ROWB;
 #pragma unroll
@@ -481,7 +482,6 @@ void fwd_mfma_kernel(FwdParams p) {
         int cv, nv;
         int cur = next_block(0, cv);
         int nxt = cur < nkb ? next_block(cur + 1, nv) : nkb;
-        if (QLDS) q_copy();
         if (cur < nkb) load_tile(cur, KB[0], VB[0]);
         kv_barrier<0>();
         if (QLDS) {
@@ -502,7 +502,6 @@ void fwd_mfma_kernel(FwdParams p) {
             if (cur < nkb) nxt = next_block(cur + 1, nv);
         }
     } else {
-        if (QLDS) q_copy();
         if (kt_lo < kt_hi) load_tile(kt_lo, KB[0], VB[0]);
         kv_barrier<0>();
         if (QLDS) {
