@@ -329,7 +329,7 @@ mm_status mm_attn_bwd(const mm_bwd_args *a, void *stream) {
     p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Sq = a->Sq; p.Skv = a->Skv; p.group = a->Hq / a->Hkv;
     p.sq_pad = (a->Sq + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad;
     p.ws_lse2 = (float *)a->workspace;
-    p.ws_dd = p.ws_lse2 + (int64_t)a->B * a->Hq * p.sq_pad;
+    p.ws_nd = p.ws_lse2 + (int64_t)a->B * a->Hq * p.sq_pad;
     p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_ss = a->q_strides[2];
     p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_ss = a->k_strides[2];
     p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_ss = a->v_strides[2];

@@ -22,7 +22,8 @@
 
 namespace mm {
 
-// ---- D_i = dO_i . O_i and lse2_i = LSE_i * log2(e) (+inf when LSE_i = -inf) ----
+// ---- -D_i = -(dO_i . O_i) and lse2_i = LSE_i * log2(e) (+inf when LSE_i = -inf) ----
+// (-D: the dK/dV kernel starts its dP accumulators at it, so its MFMAs give dP - D)
 template <typename TT, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     constexpr int LPR = D / 8;  // lanes per row, 8 elements each
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (rid < nrows && c == 0) {
         const int64_t w = (rid / p.Sq) * p.sq_pad + rid % p.Sq;
-        p.ws_dd[w] = acc;
+        p.ws_nd[w] = -acc;
         const float l = p.lse[rid];
         p.ws_lse2[w] = l == -INFINITY ? INFINITY : l * kLog2e;
     }
@@ -102,7 +103,7 @@ void bwd_dq_kernel(BwdParams p) {
     }
     const int64_t wid = ((int64_t)b * p.Hq + h) * p.sq_pad + (row_ok ? row : 0);
     const float lse2 = row_ok ? p.ws_lse2[wid] : INFINITY;
-    const float ddr = row_ok ? p.ws_dd[wid] : 0.f;
+    const float ndr = row_ok ? p.ws_nd[wid] : 0.f;  // -D
 
     const int row_max = min(q0 + BM, p.Sq) - 1;
     int j_lo = 0, j_hi = p.Skv;
@@ -264,7 +265,7 @@ void bwd_dq_kernel(BwdParams p) {
                         } else {
                             pv = fast_exp2(fmaf(sacc[e], c2, -lse2));
                         }
-                        x[u] = pv * (dpacc[e] - ddr);
+                        x[u] = pv * (dpacc[e] + ndr);
                     }
                     dsp[e2] = pack2(x[0], x[1], TT{});
                 }
@@ -355,7 +356,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILEB, "tile shape");
     static_assert(kBwdRowPad % BQ == 0, "workspace row padding");
 
-    // per stage: Q tile, dO tile, then the tile rows' lse2 and D (64 floats each), and
+    // per stage: Q tile, dO tile, then the tile rows' lse2 and -D (64 floats each), and
     // with the document mask their 64 query document ids (read from LDS by the tile: a
     // global load inside it would make the compiler wait for the copy in flight)
     constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4 + ((MASK & MASK_DOC) ? BQ * 4 : 0);
@@ -451,11 +452,11 @@ void bwd_dkdv_kernel(BwdParams p) {
         const uint32_t ql = lds_addr(dst) + (uint32_t)(wave_s * LOADS) * 1024u;
         const uint32_t dl = ql + TILEB;
         if (wave_s == 0) {
-            // the rows' lse2 and D (the (b, h) row block is padded to whole tiles)
+            // the rows' lse2 and -D (the (b, h) row block is padded to whole tiles)
             const int64_t w = ((int64_t)b * p.Hq + h) * p.sq_pad + i0 + lane;
             const uint32_t sl = lds_addr(dst) + 2 * TILEB;
             dma4_vaddr(p.ws_lse2 + w, sl);
-            dma4_vaddr(p.ws_dd + w, sl + BQ * 4);
+            dma4_vaddr(p.ws_nd + w, sl + BQ * 4);
             // the rows' document ids, clamped to the last row
             if (MASK & MASK_DOC) dma4_vaddr(p.qdoc + b * p.qdoc_sb + min(i0 + lane, p.Sq - 1), sl + 2 * BQ * 4);
         }
@@ -517,22 +518,22 @@ void bwd_dkdv_kernel(BwdParams p) {
         int dfirst = 0, dend = BQ;
         if ((MASK & MASK_DOC) && doc_mask) tile_doc_range(qd[lane], mykdoc, dfirst, dend);
         // per-lane rows of block rb of the accumulator: i0 + 32*rb + 8*a + 4*hi + (0..3),
-        // their lse2 and D from the copy in LDS (pad rows hold no data and are masked)
-        const float *sl2 = (const float *)(Qt + 2 * TILEB), *sdd = sl2 + BQ;
-        f32x4 l2[RB][4], dd[RB][4];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                l2[rb][a] = *(const f32x4 *)(sl2 + 32 * rb + 8 * a + 4 * hi);
-                dd[rb][a] = *(const f32x4 *)(sdd + 32 * rb + 8 * a + 4 * hi);
-            }
-        // S = Q K^T and dP = dO V^T (a lane: one key, 16 rows per 32-row block)
+        // their lse2 and -D from the copy in LDS (pad rows hold no data and are masked)
+        const float *sl2 = (const float *)(Qt + 2 * TILEB), *snd = sl2 + BQ;
+        f32x4 l2[RB][4];
+        // S = Q K^T and dP - D = dO V^T - D (a lane: one key, 16 rows per 32-row block;
+        // the dP accumulators start at the rows' -D)
         f32x16 sacc[RB], dpacc[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             sacc[rb] = f32x16{};
-            dpacc[rb] = f32x16{};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                l2[rb][a] = *(const f32x4 *)(sl2 + 32 * rb + 8 * a + 4 * hi);
+                const f32x4 nd = *(const f32x4 *)(snd + 32 * rb + 8 * a + 4 * hi);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dpacc[rb][4 * a + c] = nd[c];
+            }
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -590,10 +591,10 @@ void bwd_dkdv_kernel(BwdParams p) {
                             const float t = ALIBI ? fmaf(sacc[rb][e], c2, slope2 * (float)(key - i)) : sacc[rb][e] * c2;
                             const bool keep = !masked || (uint32_t)(io - ilo) < span;
                             x = keep ? fast_exp2(t - lse2) : 0.f;
-                            ds[u] = keep ? x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]) : 0.f;
+                            ds[u] = keep ? x * dpacc[rb][e] : 0.f;
                         } else {
                             x = fast_exp2(fmaf(sacc[rb][e], c2, -lse2));
-                            ds[u] = x * (dpacc[rb][e] - dd[rb][e >> 2][e & 3]);
+                            ds[u] = x * dpacc[rb][e];
                         }
                         pv[u] = x;
                     }

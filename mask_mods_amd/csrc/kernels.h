@@ -48,7 +48,7 @@ struct BwdParams {
     const float *lse;      // forward LSE, natural log, [B, Hq, Sq] contiguous
     void *dq, *dk, *dv;
     float *ws_lse2;        // [B, Hq, sq_pad]: LSE * log2(e), +inf for rows with no kept key
-    float *ws_dd;          // [B, Hq, sq_pad]: rowsum(dO * O)
+    float *ws_nd;          // [B, Hq, sq_pad]: -D = -rowsum(dO * O)
     int B, Hq, Hkv, Sq, Skv, group;
     int sq_pad;            // Sq rounded up to a multiple of kBwdRowPad (rows of the workspace arrays)
     int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
