@@ -324,17 +324,10 @@ void bwd_dq_kernel(BwdParams p) {
         }
     }
 
-    if (row_ok) {
-        uint16_t *og = (uint16_t *)p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)row * p.dq_ss;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 x = {dqacc[db][4 * g4 + 0] * p.scale, dqacc[db][4 * g4 + 1] * p.scale,
-                                 dqacc[db][4 * g4 + 2] * p.scale, dqacc[db][4 * g4 + 3] * p.scale};
-                *(typename TT::vec4 *)(og + 32 * db + 8 * g4 + 4 * hi) = cvt4(x, TT{});
-            }
-    }
+    // dQ through LDS (every wave is past its last tile): each wave's own 32-row slice
+    store_rows_via_lds<TT, D>(dqacc, p.scale, (wave_s < 4 ? kv0 : kv1) + (wave_s & 3) * 32 * TL::ROWB,
+                              (uint16_t *)p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)r0 * p.dq_ss, p.dq_ss,
+                              p.Sq - r0, lane);
 }
 
 // ---- dK, dV: one workgroup = NW waves x 32 keys of one (b, kv head) ----
@@ -685,19 +678,33 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
     }
 
-    // accumulator layout: lane holds dim 32*db + l32, keys kw0 + 8*(e/4) + 4*hi + e%4
-    uint16_t *dkg = (uint16_t *)p.dk + b * p.dk_sb + hk * p.dk_sh;
-    uint16_t *dvg = (uint16_t *)p.dv + b * p.dv_sb + hk * p.dv_sh;
+    // accumulator layout: lane holds dim 32*db + l32, keys kw0 + 8*(e/4) + 4*hi + e%4.
+    // dK, then dV, go through the wave's own 32-key slice of LDS (every wave is past its
+    // last tile) in the Q tile layout and leave as whole rows, 16 bytes per lane, instead
+    // of 2 bytes per lane and store
+    unsigned char *os = qd0 + wave_s * 32 * TL::ROWB;
+    constexpr int RPS = 64 / TL::CH;  // rows per store instruction
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int t = 0; t < 2; ++t) {
+        const f32x16 *acc = t == 0 ? dkacc : dvacc;
+        const float mul = t == 0 ? p.scale : 1.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int j = kw0 + 8 * (e >> 2) + 4 * hi + (e & 3);
-            if (j < p.Skv) {
-                dkg[(int64_t)j * p.dk_ss + 32 * db + l32] = narrow1(dkacc[db][e] * p.scale, TT{});
-                dvg[(int64_t)j * p.dv_ss + 32 * db + l32] = narrow1(dvacc[db][e], TT{});
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int kk = 8 * (e >> 2) + 4 * hi + (e & 3), d = 32 * db + l32;
+                *(uint16_t *)(os + TL::off(kk, d >> 3) + 2 * (d & 7)) = narrow1(acc[db][e] * mul, TT{});
             }
+        uint16_t *g = t == 0 ? (uint16_t *)p.dk + b * p.dk_sb + hk * p.dk_sh + (int64_t)kw0 * p.dk_ss
+                             : (uint16_t *)p.dv + b * p.dv_sb + hk * p.dv_sh + (int64_t)kw0 * p.dv_ss;
+        const int64_t ss = t == 0 ? p.dk_ss : p.dv_ss;
+#pragma unroll
+        for (int i = 0; i < 32 / RPS; ++i) {
+            const int rr = i * RPS + lane / TL::CH, c = lane % TL::CH;
+            const u32x4 y = *(const u32x4 *)(os + TL::off(rr, c));
+            if (kw0 + rr < p.Skv) *(u32x4 *)(g + (int64_t)rr * ss + 8 * c) = y;
         }
+    }
 }
 
 template <typename TT, int D, bool A, int M>

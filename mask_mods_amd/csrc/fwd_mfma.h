@@ -529,29 +529,10 @@ void fwd_mfma_kernel(FwdParams p) {
     }
     const bool live = l_tot > 0.f && !dropped;
     const float inv = live ? 1.f / l_tot : 0.f;
-    // O through LDS (every wave is past its last tile): the wave writes its 32 rows into
-    // its own 32-row slice in the K tile layout, then stores whole rows, 16 bytes per lane
-    // (a lane's own fragments are 8 bytes in each of 32 rows per store instruction)
-    unsigned char *os = (wave_s < 4 ? kv0 : kv1) + (wave_s & 3) * 32 * TL::ROWB;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 x = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
-                             oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-            *(typename TT::vec4 *)(os + TL::off(l32, 4 * db + g4) + 8 * hi) = cvt4(x, TT{});
-        }
-    }
-    {
-        constexpr int RPS = 64 / TL::CH;  // rows per store instruction
-        uint16_t *ob = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh;
-#pragma unroll
-        for (int i = 0; i < 32 / RPS; ++i) {
-            const int rr = i * RPS + lane / TL::CH, c = lane % TL::CH;
-            const u32x4 y = *(const u32x4 *)(os + TL::off(rr, c));
-            if (r0 + rr < p.Sq) *(u32x4 *)(ob + (int64_t)(r0 + rr) * p.o_ss + 8 * c) = y;
-        }
-    }
+    // O through LDS (every wave is past its last tile): each wave's own 32-row slice
+    store_rows_via_lds<TT, D>(oacc, inv, (wave_s < 4 ? kv0 : kv1) + (wave_s & 3) * 32 * TL::ROWB,
+                              (uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)r0 * p.o_ss, p.o_ss,
+                              p.Sq - r0, lane);
     if (row < p.Sq && hi == 0 && p.lse)
         p.lse[((int64_t)b * p.Hq + h) * p.Sq + row] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
