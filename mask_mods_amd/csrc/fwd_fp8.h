@@ -26,6 +26,7 @@
 #pragma once
 
 #include "fwd_common.h"
+#include "fwd_tile.h"
 
 namespace mm {
 
@@ -82,6 +83,9 @@ void fwd_fp8_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILEB + DOCB];
     __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILEB + DOCB];
     __shared__ __attribute__((aligned(1024))) unsigned char kv2[2 * TILEB + DOCB];
+    // the epilogue stages each wave's 32 rows of bf16 O (TILEB bytes) through LDS, two
+    // waves per stage; 8-wave workgroups need a fourth region (one workgroup per CU)
+    __shared__ __attribute__((aligned(1024))) unsigned char kv3[NW > 6 ? 2 * TILEB : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -556,21 +560,15 @@ void fwd_fp8_kernel(FwdParams p) {
     }
     const bool live = l_tot > 0.f && !dropped;
     const float inv = live ? p.v_descale / l_tot : 0.f;
-    if (row < p.Sq) {
-        uint16_t *og = (uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 x = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
-                                 oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-                *(bf16x4 *)(og + 32 * db + 8 * g4 + 4 * hi) = cvt4(x, BF16{});
-            }
-        }
-        if (hi == 0 && p.lse) {
-            p.lse[((int64_t)b * p.Hq + h) * p.Sq + row] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-        }
-    }
+    // O through LDS as whole rows, each wave in its own TILEB-byte slice, once every wave
+    // is past its last tile
+    __syncthreads();
+    unsigned char *const os = wave_s < 2 ? kv0 : wave_s < 4 ? kv1 : wave_s < 6 ? kv2 : kv3;
+    store_rows_via_lds<BF16, D>(oacc, inv, os + (wave_s & 1) * TILEB,
+                                (uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)r0 * p.o_ss, p.o_ss,
+                                p.Sq - r0, lane);
+    if (row < p.Sq && hi == 0 && p.lse)
+        p.lse[((int64_t)b * p.Hq + h) * p.Sq + row] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool A, int M>
