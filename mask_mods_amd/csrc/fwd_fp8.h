@@ -108,9 +108,24 @@ void fwd_fp8_kernel(FwdParams p) {
     const int r0 = q0 + wave_s * 32;  // first row of this wave
     const int row = r0 + l32;
 
-    // Q^T fragments (B operand): row `row`, dims 64*c + 32*hi .. +31
+    // Q^T fragments (B operand): row `row`, dims 64*c + 32*hi .. +31. 4-wave workgroups
+    // copy their 128 rows (clamped to the last row) by DMA into stage kv2, whole rows per
+    // instruction, as two 64-row tiles in the K tile layout; the copy is in flight during
+    // the document search and the first K/V copies, and the waves read their fragments
+    // after the first barrier (the pass's first body refills kv2 only after a second one)
+    constexpr bool QLDS = NW == 4;
     i32x8 qf[NC];
-    {
+    if (QLDS) {
+        constexpr int KB8 = (64 * Tile8<D>::ROWB) / 1024, NQ = 2 * KB8 / NW, RPB = 1024 / Tile8<D>::ROWB;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int blk = wave_s * NQ + i, t2 = blk / KB8;
+            const int r = (blk % KB8) * RPB + lane / Tile8<D>::CH;
+            const int gr = min(q0 + 64 * t2 + r, p.Sq - 1);
+            dma16_vaddr(qg + (int64_t)gr * p.q_ss + 16 * ((lane % Tile8<D>::CH) ^ Tile8<D>::swz(r)),
+                        lds_addr(kv2) + (uint32_t)(blk * 1024));
+        }
+    } else {
         const bool ok = row < p.Sq;
         const uint8_t *qr = qg + (int64_t)(ok ? row : 0) * p.q_ss + 32 * hi;
 #pragma unroll
@@ -492,6 +507,16 @@ void fwd_fp8_kernel(FwdParams p) {
             load_tile(cur, kv0);
             load_tile(nxt < END ? nxt : cur, kv1);
             kv_barrier<0>();
+            if (QLDS) {
+                const unsigned char *qs = kv2 + wave_s * 32 * TL::ROWB;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const u32x4 x0 = *(const u32x4 *)(qs + koff[c][0]), x1 = *(const u32x4 *)(qs + koff[c][1]);
+                    qf[c] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                  (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                }
+                kv_barrier<0>();
+            }
             f32x16 s_cur[NKB];
             qk(kv0, s_cur);
             float cc_cur = transform(cur, c_cur, kv0, s_cur);
@@ -561,8 +586,8 @@ void fwd_fp8_kernel(FwdParams p) {
     const bool live = l_tot > 0.f && !dropped;
     const float inv = live ? p.v_descale / l_tot : 0.f;
     // O through LDS as whole rows, each wave in its own TILEB-byte slice, once every wave
-    // is past its last tile
-    __syncthreads();
+    // is past its last tile (the wait also covers the Q copy of a workgroup with no tile)
+    kv_barrier<0>();
     unsigned char *const os = wave_s < 2 ? kv0 : wave_s < 4 ? kv1 : wave_s < 6 ? kv2 : kv3;
     store_rows_via_lds<BF16, D>(oacc, inv, os + (wave_s & 1) * TILEB,
                                 (uint16_t *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)r0 * p.o_ss, p.o_ss,
