@@ -508,6 +508,16 @@ def main():
                 ent["frac_fp8_peak"] = round(alg / t / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4)
             ent["latency_vs_no_mod"] = round(t / fwd_avg_s, 3)
             cases[name] = ent
+        # the sliding window ∧ causal at widths from 0 (one key per row: the launch then
+        # only streams Q, K, V and O through HBM once) to 4096: the banded cases' floor
+        ladder = {}
+        for Wl in (0, 64, 256, 1024, 4096):
+            kw = dict(window=Wl, mask_flags=mm.MASK_CAUSAL)
+            t = time_calls(torch, stream, lambda kw=kw: mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw))
+            ladder[str(Wl)] = {"us": round(t * 1e6, 1),
+                               "tflops_algorithmic": round(4.0 * B * H * D * window_pairs(S, Wl) / t / 1e12, 1),
+                               "hbm_tb_s_min_traffic": round(4.0 * B * H * S * D * 2 / t / 1e12, 2)}
+        cases["sliding_window_ladder"] = ladder
 
     # ---- the dense workload's shorter lengths with every flex case (S 2048 and 4096), and
     # the D 64 variant (S 2048 and 8192): the pages' tables report each case at each length
