@@ -541,7 +541,7 @@ void fwd_mfma_kernel(FwdParams p) {
 constexpr int kFwdNW = 8;          // waves per workgroup without a mask mod
 constexpr int kFwdNWMasked = 4;    // window, document or block masks: finer row tiles skip more keys
 constexpr int kFwdNWCausal = 8;    // causal alone on long rows: the shared tiles outweigh the idle diagonal waves
-constexpr int kFwdCausalShort = 4096;  // causal, D = 128: at most this many visible keys -> 4 waves
+constexpr int kFwdCausalShort = 4096;  // causal without a score_mod, D = 128: at most this many visible keys -> 4 waves
 
 template <typename TT, int D, bool A, int M, int NW>
 hipError_t launch_fwd_mfma_nw(FwdParams p, hipStream_t s) {
@@ -563,15 +563,16 @@ template <typename TT, int D, bool A, int M>
 hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
     // 8 waves (256 rows) share each K/V tile and halve the L2 -> LDS traffic. Causal
     // alone at D = 128 keeps 8 on long rows (at S = 8192 as fast as 4 without a
-    // score_mod, 3% faster with alibi) but takes 4 when at most 4096 keys are visible
-    // (S 2048 and 4096: 5-6% faster, 10-15% with alibi: the finer tiles idle less past
-    // the diagonal); with a window or documents, 4-wave tiles (128 rows) follow the band
+    // score_mod, 3% faster with alibi); without a score_mod it takes 4 when at most 4096
+    // keys are visible (S 2048 and 4096: within 1% of the software-pipelined 8-wave
+    // kernel), with alibi it keeps 8 there as well (3-9% faster than 4); with a window
+    // or documents, 4-wave tiles (128 rows) follow the band
     // more closely and skip more key tiles, which matters more; a block mask's q-blocks
     // are 128 rows, one 4-wave workgroup each. D = 64 always takes 4: its halved tile
     // products leave the shared copies less to gain (no mod 7-15% faster at S 2048 to
     // 8192, causal 6-15%, alibi 0-3%)
     constexpr int NW = D == 64 ? 4 : (M == 0 ? kFwdNW : (M == MASK_CAUSAL ? kFwdNWCausal : kFwdNWMasked));
-    if (M == MASK_CAUSAL && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= kFwdCausalShort)
+    if (M == MASK_CAUSAL && !A && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= kFwdCausalShort)
         return launch_fwd_mfma_nw<TT, D, A, M, 4>(p, s);
     return launch_fwd_mfma_nw<TT, D, A, M, NW>(p, s);
 }
