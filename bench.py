@@ -537,7 +537,10 @@ def main():
                 t_nomod = None
                 for cname in names:
                     kw = short[cname]
-                    t = time_calls(torch, stream, lambda: mm.attn_fwd(sq_, sk_, sv_, ss_, out=sout, lse=slse, **kw))
+                    # the pages' report method: a call here is 40-1400 us, so 20 calls would
+                    # time a window short enough for clock ramps and the previous case to show
+                    st = pages_stats(torch, stream, lambda: mm.attn_fwd(sq_, sk_, sv_, ss_, out=sout, lse=slse, **kw))
+                    t = st["mean_us"] * 1e-6
                     dense = fwd_flops(B, H, Ss, Ss, Ds)
                     if cname in ("causal", "causal_via_mask"):
                         alg = dense / 2
@@ -547,7 +550,8 @@ def main():
                         alg = dense
                     t_nomod = t if cname == "no_mod" else t_nomod
                     scases[f"d{Ds}_s{Ss}_{cname}"] = {
-                        "us": round(t * 1e6, 1), "tflops_dense_equiv": round(dense / t / 1e12, 1),
+                        "us": round(t * 1e6, 1), "std_us": st["std_us"], "cv_pct": st["cv_pct"],
+                        "tflops_dense_equiv": round(dense / t / 1e12, 1),
                         "tflops_algorithmic": round(alg / t / 1e12, 1),
                         "frac_bf16_peak": round(alg / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                         "latency_vs_no_mod": round(t / t_nomod, 3) if t_nomod else None}
@@ -625,6 +629,8 @@ def main():
         "cases_dense_short": ({"workload": "fwd bf16 B2 H32 +LSE: D128 at Sq=Skv 2048 and 4096 with every flex "
                                            "case, D64 at 2048 and 8192; causal half-counted, sliding window "
                                            "over visited pairs",
+                               "method": f"{PAGES_WARMUP} warmup, {PAGES_SAMPLES} samples x {PAGES_ITERS} "
+                                         "calls per case (mean, std)",
                                **scases} if scases else {}),
         "cases_gqa_cross": {"workload": "fwd B2 Hq32 Hkv8 D128 Sq1024 Skv8192, ~5% of query rows dropped "
                                         "by a hash mask_mod; _window adds |i-j|<=256 AND j<=i (top-left)",
