@@ -479,16 +479,10 @@ def main():
         for name, kw in specs.items():
             kw = dict(kw)
             qq, kk, vv = kw.pop("q", q), kw.pop("k", k), kw.pop("v", v)
-            for _ in range(5):
-                mm.attn_fwd(qq, kk, vv, scale, out=out, lse=lse, **kw)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            n = 20
-            e0.record(stream)
-            for _ in range(n):
-                mm.attn_fwd(qq, kk, vv, scale, out=out, lse=lse, **kw)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) / n * 1e-3
+            # the pages' report method (a 20-call window showed the first case after the
+            # headline runs up to 8% slower than the same kernel timed later)
+            st = pages_stats(torch, stream, lambda: mm.attn_fwd(qq, kk, vv, scale, out=out, lse=lse, **kw))
+            t = st["mean_us"] * 1e-6
             dense = fwd_flops(B, H, S, S, D)
             if name in ("causal", "causal_via_mask", "block_causal", "fp8_causal"):
                 alg = dense / 2
@@ -500,7 +494,8 @@ def main():
                 alg = 4.0 * D * doc_pairs  # kept pairs summed over (b, h)
             else:
                 alg = dense
-            ent = {"us": round(t * 1e6, 1), "tflops_dense_equiv": round(dense / t / 1e12, 1),
+            ent = {"us": round(t * 1e6, 1), "std_us": st["std_us"], "cv_pct": st["cv_pct"],
+                   "tflops_dense_equiv": round(dense / t / 1e12, 1),
                    "tflops_algorithmic": round(alg / t / 1e12, 1)}
             if name == "causal":
                 ent["tflops_causal_half"] = round(dense / 2 / t / 1e12, 1)
@@ -518,6 +513,8 @@ def main():
                                "tflops_algorithmic": round(4.0 * B * H * D * window_pairs(S, Wl) / t / 1e12, 1),
                                "hbm_tb_s_min_traffic": round(4.0 * B * H * S * D * 2 / t / 1e12, 2)}
         cases["sliding_window_ladder"] = ladder
+        cases["method"] = (f"flex cases: {PAGES_WARMUP} warmup, {PAGES_SAMPLES} samples x {PAGES_ITERS} calls "
+                           "(mean, std); window ladder: 20 calls after 5 warmup")
 
     # ---- the dense workload's shorter lengths with every flex case (S 2048 and 4096), and
     # the D 64 variant (S 2048 and 8192): the pages' tables report each case at each length
