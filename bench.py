@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 MFMA_FP8_PEAK_TFLOPS = 5033.2    # twice the bf16 rate (dense fp8)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+SETTLE_S = 0.5                   # untimed headline steps before any timing (clock settle)
 PAGES_NO_MOD_MI300X_TFLOPS = 470.1  # FlyDSL PR #931 report, no_mod at this workload (MI300X)
 
 FWD = dict(B=2, H=32, S=8192, D=128)
@@ -413,11 +414,20 @@ def main():
         mm.attn_decode(dq, dk, dv, L, dscale, mask=dmask, workspace=ws, out=dout, lse=dlse)
 
     stream = torch.cuda.current_stream(dev)
-    # the pages' report method on the two headline calls first: mean +- std over 12
-    # samples of 100 calls after 10 warmup calls, and the coefficient of variation. Its
-    # ~2.5 s of back-to-back calls also bring the GPU clock to its loaded steady state,
-    # which takes longer than a few warmup steps (with 5 warmup steps and nothing before
-    # them the timed steps read about 3% slow and 7x as spread)
+    # Untimed: SETTLE_S seconds of headline steps bring the GPU clock to its loaded steady
+    # state, which takes longer than a few steps (started cold with 5 warmup steps, the
+    # timed steps read about 3% slow and 7x as spread; the report method's first samples
+    # likewise)
+    settle_steps = 0
+    t_settle = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_settle:
+        for _ in range(10):
+            fwd()
+            dec()
+        settle_steps += 10
+        torch.cuda.synchronize()
+    # the pages' report method on the two headline calls: mean +- std over 12 samples of
+    # 100 calls after 10 warmup calls, and the coefficient of variation
     fwd_pages = pages_stats(torch, stream, fwd)
     dec_pages = pages_stats(torch, stream, dec)
 
@@ -601,6 +611,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": {"seconds": SETTLE_S, "steps": settle_steps,
+                   "note": "untimed headline steps before the report method and the warmup"},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
