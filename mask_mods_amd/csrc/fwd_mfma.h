@@ -572,8 +572,9 @@ hipError_t launch_fwd_mfma_one(FwdParams p, hipStream_t s) {
     // products leave the shared copies less to gain (no mod 7-15% faster at S 2048 to
     // 8192, causal 6-15%, alibi 0-3%)
     constexpr int NW = D == 64 ? 4 : (M == 0 ? kFwdNW : (M == MASK_CAUSAL ? kFwdNWCausal : kFwdNWMasked));
-    if (M == MASK_CAUSAL && !A && NW != 4 && (p.Sq < p.Skv ? p.Sq : p.Skv) <= kFwdCausalShort)
-        return launch_fwd_mfma_nw<TT, D, A, M, 4>(p, s);
+    if constexpr (M == MASK_CAUSAL && !A && NW != 4) {
+        if ((p.Sq < p.Skv ? p.Sq : p.Skv) <= kFwdCausalShort) return launch_fwd_mfma_nw<TT, D, A, M, 4>(p, s);
+    }
     return launch_fwd_mfma_nw<TT, D, A, M, NW>(p, s);
 }
 
