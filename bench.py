@@ -321,6 +321,19 @@ def profile_one(args, torch, mm, inputs, dev):
         fn = lambda: mm.attn_bwd(q, k, v, out, lse, dout, scale, workspace=ws,
                                  dq=grads[0], dk=grads[1], dv=grads[2])
         unit_bytes = 8 * B * H * S * D * 2 + 2 * B * H * S * 4  # q k v o dO in, dq dk dv out, lse
+    elif args.only in ("window", "causal2048"):
+        # the banded forward (WINDOW(256) AND causal at the headline shape) and the short
+        # causal forward (S 2048), for their own counter passes
+        B, H, D = FWD["B"], FWD["H"], FWD["D"]
+        S = FWD["S"] if args.only == "window" else 2048
+        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        kw = dict(window=256, mask_flags=mm.MASK_CAUSAL) if args.only == "window" else dict(causal=True)
+        fn = lambda: mm.attn_fwd(q, k, v, scale, out=out, lse=lse, **kw)
+        unit_bytes = fwd_bytes(B, H, S, D)
     elif args.only == "fwd":
         B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
         x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
@@ -360,7 +373,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--only", choices=["fwd", "fp8", "bwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fp8", "bwd", "decode", "copy", "window", "causal2048"], default=None,
                     help="profiling aid: run just one kernel family (or a plain 1 GiB device copy "
                          "used to calibrate the HBM byte counters) and print its timing")
     ap.add_argument("--ingest", metavar="DIR", default=None,
