@@ -15,7 +15,7 @@ mixed-length batch of 8; the backward; and the CPU oracle timed on a bounded sam
 of the forward workload, on the tiny fp32 workload and on the full decode call, on
 this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--seed N] [--gpus 1] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -36,6 +36,12 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/C
 MFMA_FP8_PEAK_TFLOPS = 5033.2    # twice the bf16 rate (dense fp8)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 SETTLE_S = 0.5                   # untimed headline steps before any timing (clock settle)
+SEED = 0                         # --seed: added to every input seed of the run
+
+
+def sd(n: int) -> int:
+    """The run's seed for input stream n (the same streams as with --seed 0, shifted)."""
+    return n + SEED
 PAGES_NO_MOD_MI300X_TFLOPS = 470.1  # FlyDSL PR #931 report, no_mod at this workload (MI300X)
 
 FWD = dict(B=2, H=32, S=8192, D=128)
@@ -101,7 +107,7 @@ def cpu_configs(xd):
     import oracle
     from mask_mods_amd import inputs
     out = {}
-    x = inputs.attention_inputs(0, 1, 2, 2, 128, 128, 64, "f32")
+    x = inputs.attention_inputs(sd(0), 1, 2, 2, 128, 128, 64, "f32")
     args = [inputs.bits_to_f64(x[n], "f32") for n in ("q", "k", "v")]
     t0 = time.perf_counter()
     for _ in range(10):
@@ -125,7 +131,7 @@ def cpu_baseline(x, target_s=10.0, xd=None):
     B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
     qd, kd, vd = (inputs.bits_to_f64(x[n], "bf16") for n in ("q", "k", "v"))
     scale = float(np.float32(1.0 / math.sqrt(D)))
-    g = np.random.default_rng(123)
+    g = np.random.default_rng(sd(123))
     threads = oracle.max_threads()
     probe = g.integers(0, B * H * S, size=4096)
     t0 = time.perf_counter()
@@ -300,7 +306,7 @@ def profile_one(args, torch, mm, inputs, dev):
         unit_bytes = 2 * n
     elif args.only == "fp8":
         B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
-        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        x = inputs.attention_inputs(sd(2), B, H, H, S, S, D, "bf16")
         q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
         (q8, sq), (k8, sk), (v8, sv) = (to_fp8(t, torch) for t in (q, k, v))
         out = torch.empty_like(q)
@@ -310,11 +316,11 @@ def profile_one(args, torch, mm, inputs, dev):
         unit_bytes = fp8_bytes(B, H, S, D)
     elif args.only == "bwd":
         B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
-        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        x = inputs.attention_inputs(sd(2), B, H, H, S, S, D, "bf16")
         q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
         scale = float(np.float32(1.0 / math.sqrt(D)))
         out, lse = mm.attn_fwd(q, k, v, scale)
-        g = np.random.default_rng(11)
+        g = np.random.default_rng(sd(11))
         dout = torch.from_numpy(g.standard_normal((B, H, S, D), dtype=np.float32)).to(dev).bfloat16()
         ws = torch.empty(mm.bwd_workspace_size(B, H, S) // 4 + 4, dtype=torch.float32, device=dev)
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
@@ -326,7 +332,7 @@ def profile_one(args, torch, mm, inputs, dev):
         # causal forward (S 2048), for their own counter passes
         B, H, D = FWD["B"], FWD["H"], FWD["D"]
         S = FWD["S"] if args.only == "window" else 2048
-        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        x = inputs.attention_inputs(sd(2), B, H, H, S, S, D, "bf16")
         q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
         out = torch.empty_like(q)
         lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
@@ -336,7 +342,7 @@ def profile_one(args, torch, mm, inputs, dev):
         unit_bytes = fwd_bytes(B, H, S, D)
     elif args.only == "fwd":
         B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
-        x = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+        x = inputs.attention_inputs(sd(2), B, H, H, S, S, D, "bf16")
         q, k, v = (dev_tensor(x[n], "bf16") for n in ("q", "k", "v"))
         out = torch.empty_like(q)
         lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
@@ -345,7 +351,7 @@ def profile_one(args, torch, mm, inputs, dev):
         unit_bytes = fwd_bytes(B, H, S, D)
     else:
         Bd, Hd, L, Dd = DEC["B"], DEC["H"], DEC["L"], DEC["D"]
-        x = inputs.decode_inputs(1, Bd, Hd, Hd, [L], Dd, "f16")
+        x = inputs.decode_inputs(sd(1), Bd, Hd, Hd, [L], Dd, "f16")
         dq, dk, dv, dm = (dev_tensor(x[n], "f16") for n in ("q", "k", "v", "mask"))
         ws = torch.empty(mm.decode_workspace_size(Bd, Hd, L, Dd) // 4 + 4, dtype=torch.float32, device=dev)
         fn = lambda: mm.attn_decode(dq, dk, dv, L, 0.08837890625, mask=dm, workspace=ws)
@@ -370,6 +376,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--seed", type=int, default=0, help="offset added to every input seed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -381,6 +388,8 @@ def main():
     args = ap.parse_args()
     if args.ingest:
         return ingest(args.ingest)
+    global SEED
+    SEED = args.seed
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(attention shards by (batch, head) with no exchange between GPUs, so each "
@@ -404,14 +413,14 @@ def main():
 
     # ---- inputs (seeded, synthetic), resident in HBM
     B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
-    xf = inputs.attention_inputs(2, B, H, H, S, S, D, "bf16")
+    xf = inputs.attention_inputs(sd(2), B, H, H, S, S, D, "bf16")
     q, k, v = (dev_tensor(xf[n], "bf16") for n in ("q", "k", "v"))
     out = torch.empty_like(q)
     lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
     scale = float(np.float32(1.0 / math.sqrt(D)))
 
     Bd, Hd, L, Dd = DEC["B"], DEC["H"], DEC["L"], DEC["D"]
-    xd = inputs.decode_inputs(1, Bd, Hd, Hd, [L], Dd, "f16")
+    xd = inputs.decode_inputs(sd(1), Bd, Hd, Hd, [L], Dd, "f16")
     dq, dk, dv = (dev_tensor(xd[n], "f16") for n in ("q", "k", "v"))
     dmask = dev_tensor(xd["mask"], "f16")
     dout = torch.empty_like(dq)
@@ -487,14 +496,14 @@ def main():
         # with half of the blocks empty (a quarter full, a quarter partial, no predicate)
         nqb, nkb = S // mm.BLOCK_Q, S // mm.BLOCK_KV
         bm_causal = mm.block_mask_create(S, S, causal=True)
-        bm_rand_np = inputs.random_block_mask(7, (B, H, nqb, nkb), p_empty=0.5, p_full=0.25)
+        bm_rand_np = inputs.random_block_mask(sd(7), (B, H, nqb, nkb), p_empty=0.5, p_full=0.25)
         bm_rand = torch.from_numpy(bm_rand_np).to(dev)
         specs["block_causal"] = dict(causal=True, block_mask=bm_causal)
         specs["block_sparse_50"] = dict(block_mask=bm_rand)
         block_pairs = int((bm_rand_np != 0).sum()) * mm.BLOCK_Q * mm.BLOCK_KV
         # document mask (packed sequences, a mask_mod over captured id tensors): 16
         # documents of random lengths per sequence, causal inside each document
-        docs_np = inputs.packed_document_ids(7, B, S, 16)
+        docs_np = inputs.packed_document_ids(sd(7), B, S, 16)
         specs["document_causal"] = dict(causal=True, q_doc=torch.from_numpy(docs_np).to(dev))
         doc_pairs = H * sum(int(n) * (int(n) + 1) // 2
                             for row in docs_np for n in np.unique(row, return_counts=True)[1])
@@ -553,7 +562,7 @@ def main():
                  "causal_via_mask": dict(mask_flags=mm.MASK_CAUSAL)}
         for Ds, lens, names in ((D, (2048, 4096), list(short)), (64, (2048, 8192), ["no_mod", "causal", "alibi"])):
             for Ss in lens:
-                xs = inputs.attention_inputs(2, B, H, H, Ss, Ss, Ds, "bf16")
+                xs = inputs.attention_inputs(sd(2), B, H, H, Ss, Ss, Ds, "bf16")
                 sq_, sk_, sv_ = (dev_tensor(xs[n], "bf16") for n in ("q", "k", "v"))
                 sout = torch.empty_like(sq_)
                 slse = torch.empty(B, H, Ss, dtype=torch.float32, device=dev)
@@ -591,7 +600,7 @@ def main():
         rd = (20240, int(0.05 * 2 ** 32))
         dense_g = fwd_flops(Bg, Hqg, Sqg, Skvg, D)
         for dt in ("bf16", "f16"):
-            xg = inputs.attention_inputs(4, Bg, Hqg, Hkvg, Sqg, Skvg, D, dt)
+            xg = inputs.attention_inputs(sd(4), Bg, Hqg, Hkvg, Sqg, Skvg, D, dt)
             gq, gk, gv = (dev_tensor(xg[n], dt) for n in ("q", "k", "v"))
             gout = torch.empty_like(gq)
             glse = torch.empty(Bg, Hqg, Sqg, dtype=torch.float32, device=dev)
@@ -624,6 +633,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "seed": args.seed,
         "settle": {"seconds": SETTLE_S, "steps": settle_steps,
                    "note": "untimed headline steps before the report method and the warmup"},
         "ms_per_step": round(ms_per_step, 4),
@@ -681,7 +691,7 @@ def main():
         # Infinity Cache cannot serve a call's K/V from the previous one
         gsets = []
         for r in range(3):
-            xg = inputs.decode_inputs(3 + r, 1, Hd, Hkv_g, [L], Dd, "f16")
+            xg = inputs.decode_inputs(sd(3 + r), 1, Hd, Hkv_g, [L], Dd, "f16")
             gsets.append(tuple(dev_tensor(xg[n], "f16") for n in ("q", "k", "v", "mask")))
         gws = torch.empty(mm.decode_workspace_size(1, Hd, L, Dd, Hkv=Hkv_g) // 4 + 4, dtype=torch.float32, device=dev)
         gcall = [0]
@@ -697,7 +707,7 @@ def main():
         del gsets
         Bp, page = 8, 64
         pages = L // page
-        gp = np.random.default_rng(5)
+        gp = np.random.default_rng(sd(5))
         perm = torch.from_numpy(gp.permutation(Bp * pages).reshape(Bp, pages).astype(np.int32)).to(dev)
         pk = torch.randn(Bp * pages, Hd, page, Dd, device=dev).half()
         pv = torch.randn_like(pk)
@@ -721,7 +731,7 @@ def main():
         # enough input sets rotate that one pass over them exceeds the 256 MB Infinity
         # Cache, so every call streams its K/V from HBM; below that the call is launch-bound.
         gen = torch.Generator(device=dev)
-        gen.manual_seed(17)
+        gen.manual_seed(sd(17))
         ladder = {}
         for Ll in (1, 17, 1000, 4096):
             per_set = dec_bytes(1, Hd, Ll, Dd)
@@ -763,7 +773,7 @@ def main():
         # a batch of 8 sequences whose KV lengths are drawn from the ladder's lengths (cache
         # capacity 32768, per-sequence lengths passed to the kernel)
         Bm = 8
-        lens_m = np.random.default_rng(29).choice([1, 17, 1000, 4096, 32768], size=Bm)
+        lens_m = np.random.default_rng(sd(29)).choice([1, 17, 1000, 4096, 32768], size=Bm)
         mk = torch.randn(Bm, Hd, L, Dd, device=dev, generator=gen).half()
         mv = torch.randn(Bm, Hd, L, Dd, device=dev, generator=gen).half()
         mq = torch.randn(Bm, Hd, 1, Dd, device=dev, generator=gen).half()
@@ -780,7 +790,7 @@ def main():
 
     # backward (bf16, same shape): dq, dk, dv of sum(dO * O) from the forward's O and LSE
     if not args.no_cases:
-        g = np.random.default_rng(11)
+        g = np.random.default_rng(sd(11))
         dout = torch.from_numpy(g.standard_normal((B, H, S, D), dtype=np.float32)).to(dev).bfloat16()
         bws = torch.empty(mm.bwd_workspace_size(B, H, S) // 4 + 4, dtype=torch.float32, device=dev)
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
