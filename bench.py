@@ -327,6 +327,22 @@ def profile_one(args, torch, mm, inputs, dev):
         fn = lambda: mm.attn_bwd(q, k, v, out, lse, dout, scale, workspace=ws,
                                  dq=grads[0], dk=grads[1], dv=grads[2])
         unit_bytes = 8 * B * H * S * D * 2 + 2 * B * H * S * 4  # q k v o dO in, dq dk dv out, lse
+    elif args.only == "gqa":
+        # GQA decode (B1 Hq32 Hkv8 L32768 D128 f16, pad mask), three input sets in rotation
+        # (408 MB, past the 256 MB Infinity Cache) as in the benchmark's case
+        Hq, Hkv, L, D = DEC["H"], 8, DEC["L"], DEC["D"]
+        sets = []
+        for r in range(3):
+            xg = inputs.decode_inputs(sd(3 + r), 1, Hq, Hkv, [L], D, "f16")
+            sets.append(tuple(dev_tensor(xg[n], "f16") for n in ("q", "k", "v", "mask")))
+        ws = torch.empty(mm.decode_workspace_size(1, Hq, L, D, Hkv=Hkv) // 4 + 4, dtype=torch.float32, device=dev)
+        calls = [0]
+
+        def fn():
+            gq, gk, gv, gm = sets[calls[0] % 3]
+            calls[0] += 1
+            mm.attn_decode(gq, gk, gv, L, 0.08837890625, mask=gm, workspace=ws)
+        unit_bytes = Hkv * L * D * 2 * 2 + Hq * L * 2 + 2 * Hq * D * 2 + Hq * 4
     elif args.only in ("window", "causal2048"):
         # the banded forward (WINDOW(256) AND causal at the headline shape) and the short
         # causal forward (S 2048), for their own counter passes
@@ -380,7 +396,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cases", action="store_true", help="skip the other flex cases")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--only", choices=["fwd", "fp8", "bwd", "decode", "copy", "window", "causal2048"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fp8", "bwd", "decode", "copy", "window", "causal2048", "gqa"], default=None,
                     help="profiling aid: run just one kernel family (or a plain 1 GiB device copy "
                          "used to calibrate the HBM byte counters) and print its timing")
     ap.add_argument("--ingest", metavar="DIR", default=None,
